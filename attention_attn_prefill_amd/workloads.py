@@ -1,0 +1,288 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module draws random numbers and lays them out; it holds none of the
+attention arithmetic.  Both the HIP path and the fp64 oracle consume the same
+binary16 arrays that it returns.
+
+Recipe:
+  * tensors: standard normal draws (NumPy ``Generator(PCG64)``, float32
+    ziggurat), rounded to binary16 (round-to-nearest-even).  Each tensor has a
+    ``SeedSequence([config_id, tensor_id, seed])``; large tensors are filled in
+    fixed 4 Mi-element chunks, chunk c using child c of that sequence, so the
+    values do not depend on the thread count.
+  * paged decode: ``seq_lens`` inclusive-uniform integers (or a fixed length);
+    ``num_blocks = sum(ceil(L/16))``; physical ids are a seeded permutation of
+    ``0..num_blocks-1`` handed out in (sequence, logical block) order; unused
+    table entries are -1.
+  * the cross-attention workload's Q and K are rotated by interleaved-pair
+    rotary embeddings (pair (2j, 2j+1) turned by ``pos * base**(-2j/D)``,
+    positions 0..T-1, base 10000) in fp64 on the host, then rounded to
+    binary16 -- the convention of the POPCORNBENCH Kimi-K2.6 trace page
+    (its RoPE discussion).  This is input preparation, not part of the path.
+  * the pages' own unit-test inputs ("Tutorial: Adding a New Kernel to
+    RL.cu", test_attention.cu: the deterministic LCG helper and the test
+    runners) are reproduced by ``pages_prefill_case`` / ``pages_decode_case``.
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_CHUNK = 1 << 22
+
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    config_id: int
+    B: int
+    S_q: int
+    S_kv: int
+    H_q: int
+    H_kv: int
+    D: int
+    causal: bool
+    rope_base: float | None = None
+
+    @property
+    def pairs(self) -> int:
+        """Unmasked (query, key) pairs: the work unit of the FLOP count."""
+        if self.causal:
+            return self.B * self.H_q * self.S_q * (self.S_q + 1) // 2
+        return self.B * self.H_q * self.S_q * self.S_kv
+
+    @property
+    def flops(self) -> int:
+        """Algorithmic flops: 2*D for Q.K plus 2*D for P.V per unmasked pair."""
+        return 4 * self.D * self.pairs
+
+    @property
+    def dense_flops(self) -> int:
+        """The pages' benchmark convention: 4*B*H_q*S_q*S_kv*D, mask ignored."""
+        return 4 * self.B * self.H_q * self.S_q * self.S_kv * self.D
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    config_id: int
+    num_seqs: int
+    H_q: int
+    H_kv: int
+    D: int
+    block_size: int
+    max_blocks_per_seq: int
+    len_lo: int
+    len_hi: int
+    extra: dict = field(default_factory=dict, compare=False)
+
+
+CONFIGS = {
+    "tiny_causal": PrefillConfig("tiny_causal", 1, 1, 64, 64, 2, 1, 128, True),
+    "cross_attn_rope": PrefillConfig("cross_attn_rope", 2, 4, 64, 128, 8, 8, 32, False,
+                                     rope_base=10000.0),
+    "qwen3_prefill": PrefillConfig("qwen3_prefill", 3, 4, 2048, 2048, 16, 8, 128, True),
+    "paged_decode": DecodeConfig("paged_decode", 4, 256, 16, 8, 128, 16, 256, 128, 4096),
+    "long_prefill": PrefillConfig("long_prefill", 5, 1, 32768, 32768, 16, 8, 128, True),
+    "long_decode": DecodeConfig("long_decode", 6, 64, 16, 8, 128, 16, 2048, 32768, 32768),
+}
+
+
+def normal_f16(shape, seed_words, threads: int = 16) -> np.ndarray:
+    """Standard-normal binary16 array, deterministic in ``seed_words``."""
+    n = int(np.prod(shape))
+    out32 = np.empty(n, np.float32)
+    out16 = np.empty(n, np.float16)
+    nchunks = max(1, (n + _CHUNK - 1) // _CHUNK)
+    children = np.random.SeedSequence(list(seed_words)).spawn(nchunks)
+
+    def fill(c):
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        g = np.random.Generator(np.random.PCG64(children[c]))
+        g.standard_normal(hi - lo, dtype=np.float32, out=out32[lo:hi])
+        out16[lo:hi] = out32[lo:hi]
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(min(threads, nchunks)) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out16.reshape(shape)
+
+
+def rope_interleaved(x16: np.ndarray, base: float) -> np.ndarray:
+    """Rotate pairs (2j, 2j+1) of the last axis by pos * base**(-2j/D).
+
+    ``x16`` is [B, T, H, D] binary16; positions are 0..T-1 along axis 1.
+    Arithmetic in fp64, result rounded to binary16.
+    """
+    B, T, H, D = x16.shape
+    x = x16.astype(np.float64)
+    inv_freq = base ** (-np.arange(0, D, 2, dtype=np.float64) / D)      # [D/2]
+    ang = np.arange(T, dtype=np.float64)[:, None] * inv_freq[None, :]   # [T, D/2]
+    c = np.cos(ang)[None, :, None, :]
+    s = np.sin(ang)[None, :, None, :]
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out.astype(np.float16)
+
+
+def prefill_inputs(cfg: PrefillConfig | str, seed: int = 0):
+    """(q, k, v) binary16 arrays for a prefill workload."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    q = normal_f16((cfg.B, cfg.S_q, cfg.H_q, cfg.D), (cfg.config_id, 0, seed))
+    k = normal_f16((cfg.B, cfg.S_kv, cfg.H_kv, cfg.D), (cfg.config_id, 1, seed))
+    v = normal_f16((cfg.B, cfg.S_kv, cfg.H_kv, cfg.D), (cfg.config_id, 2, seed))
+    if cfg.rope_base is not None:
+        q = rope_interleaved(q, cfg.rope_base)
+        k = rope_interleaved(k, cfg.rope_base)
+    return q, k, v
+
+
+def paged_layout(seq_lens, block_size: int, max_blocks_per_seq: int, seed_words):
+    """Block tables for ``seq_lens``: a seeded permutation of the physical
+    blocks, assigned in (sequence, logical block) order; unused entries -1."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    nb = (np.maximum(seq_lens, 0) + block_size - 1) // block_size
+    if nb.max(initial=0) > max_blocks_per_seq:
+        raise ValueError("a sequence needs more blocks than the table holds")
+    num_blocks = int(nb.sum())
+    perm = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(seed_words)))) \
+        .permutation(max(num_blocks, 1)).astype(np.int32)
+    bt = np.full((len(seq_lens), max_blocks_per_seq), -1, np.int32)
+    pos = 0
+    for s, n in enumerate(nb):
+        bt[s, :n] = perm[pos:pos + n]
+        pos += n
+    return bt, max(num_blocks, 1)
+
+
+def decode_inputs(cfg: DecodeConfig | str, seed: int = 0):
+    """(q, k_cache, v_cache, block_tables, seq_lens) for a paged-decode workload."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.config_id, 3, seed])))
+    seq_lens = g.integers(cfg.len_lo, cfg.len_hi, size=cfg.num_seqs, endpoint=True).astype(np.int32)
+    bt, num_blocks = paged_layout(seq_lens, cfg.block_size, cfg.max_blocks_per_seq,
+                                  (cfg.config_id, 4, seed))
+    q = normal_f16((cfg.num_seqs, cfg.H_q, cfg.D), (cfg.config_id, 0, seed))
+    shape = (num_blocks, cfg.H_kv, cfg.block_size, cfg.D)
+    k_cache = normal_f16(shape, (cfg.config_id, 1, seed))
+    v_cache = normal_f16(shape, (cfg.config_id, 2, seed))
+    return q, k_cache, v_cache, bt, seq_lens
+
+
+def kv_bytes(seq_lens, H_kv: int, D: int) -> int:
+    """Algorithmic decode traffic: K and V bytes of every visible token."""
+    return int(np.maximum(np.asarray(seq_lens, np.int64), 0).sum()) * H_kv * D * 2 * 2
+
+
+# ---- the pages' own unit-test inputs ---------------------------------------
+
+class PagesLCG:
+    """The 32-bit LCG of the pages' attention unit test (multiplier 1664525,
+    increment 1013904223, state 42), mapped to [-1, 1] in float32."""
+
+    def __init__(self, state: int = 42):
+        self.state = state & 0xFFFFFFFF
+
+    def uniform(self, n: int) -> np.ndarray:
+        states = np.empty(n, np.uint32)
+        s = self.state
+        for i in range(n):
+            s = (s * 1664525 + 1013904223) & 0xFFFFFFFF
+            states[i] = s
+        self.state = s
+        x = (states >> np.uint32(1)).astype(np.float32) / np.float32(0x7FFFFFFF)
+        return x * np.float32(2.0) - np.float32(1.0)
+
+
+def pages_prefill_case(lcg: PagesLCG, B: int, S: int, H_q: int, H_kv: int, D: int = 128):
+    """Q, K, V as the pages' prefill test draws them: U(-0.5, 0.5) in float32
+    from the shared LCG, Q then K then V, rounded to binary16."""
+    half = np.float32(0.5)
+    q = (lcg.uniform(B * S * H_q * D) * half).astype(np.float16).reshape(B, S, H_q, D)
+    k = (lcg.uniform(B * S * H_kv * D) * half).astype(np.float16).reshape(B, S, H_kv, D)
+    v = (lcg.uniform(B * S * H_kv * D) * half).astype(np.float16).reshape(B, S, H_kv, D)
+    return q, k, v
+
+
+def pages_decode_case(lcg: PagesLCG, num_seqs: int, ctx: int, H_q: int, H_kv: int,
+                      D: int = 128, block_size: int = 16):
+    """The pages' decode test: q, then K and V drawn alternately per element
+    into a contiguous [num_seqs, ctx, H_kv, D] context, paged with the identity
+    table (sequence s, logical block b -> physical s*blocks_per_seq + b)."""
+    half = np.float32(0.5)
+    q = (lcg.uniform(num_seqs * H_q * D) * half).astype(np.float16).reshape(num_seqs, H_q, D)
+    n = num_seqs * ctx * H_kv * D
+    kv = lcg.uniform(2 * n) * half
+    k = kv[0::2].astype(np.float16).reshape(num_seqs, ctx, H_kv, D)
+    v = kv[1::2].astype(np.float16).reshape(num_seqs, ctx, H_kv, D)
+    bps = (ctx + block_size - 1) // block_size
+    k_cache = np.zeros((num_seqs * bps, H_kv, block_size, D), np.float16)
+    v_cache = np.zeros_like(k_cache)
+    for s in range(num_seqs):
+        for t in range(ctx):
+            pb = s * bps + t // block_size
+            k_cache[pb, :, t % block_size, :] = k[s, t]
+            v_cache[pb, :, t % block_size, :] = v[s, t]
+    bt = (np.arange(num_seqs)[:, None] * bps + np.arange(bps)[None, :]).astype(np.int32)
+    seq_lens = np.full(num_seqs, ctx, np.int32)
+    return q, k_cache, v_cache, bt, seq_lens, k, v
+
+
+def paginate(k: np.ndarray, v: np.ndarray, seq_lens, block_size: int, max_blocks_per_seq: int,
+             seed_words=(0, 0)):
+    """Scatter contiguous per-sequence K/V [num_seqs, T, H_kv, D] into a paged
+    cache with a seeded random block permutation.  Returns
+    (k_cache, v_cache, block_tables)."""
+    num_seqs, T, H_kv, D = k.shape
+    bt, num_blocks = paged_layout(seq_lens, block_size, max_blocks_per_seq, seed_words)
+    k_cache = np.zeros((num_blocks, H_kv, block_size, D), np.float16)
+    v_cache = np.zeros_like(k_cache)
+    for s in range(num_seqs):
+        L = int(seq_lens[s])
+        for lb in range((L + block_size - 1) // block_size):
+            t0, t1 = lb * block_size, min(L, (lb + 1) * block_size)
+            pb = bt[s, lb]
+            k_cache[pb, :, : t1 - t0, :] = k[s, t0:t1].transpose(1, 0, 2)
+            v_cache[pb, :, : t1 - t0, :] = v[s, t0:t1].transpose(1, 0, 2)
+    return k_cache, v_cache, bt
+
+
+def sample_prefill_rows(cfg: PrefillConfig, n_random: int, seed: int = 0, tile: int = 128):
+    """Stratified row sample for prefill parity at full size: every (b, h) at
+    the first and last rows, rows at tile boundaries, and random rows."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.config_id, 7, seed])))
+    S = cfg.S_q
+    pos = set(range(min(4, S))) | set(range(max(0, S - 4), S))
+    for t in range(tile, S, tile):
+        pos |= {t - 1, t}
+    pos = np.array(sorted(pos), np.int64)
+    rows = []
+    for b in range(cfg.B):
+        for h in range(cfg.H_q):
+            rows.append((b * S + pos) * cfg.H_q + h)
+    rows.append(rng.integers(0, cfg.B * S * cfg.H_q, size=n_random))
+    return np.unique(np.concatenate(rows)).astype(np.int64)
+
+
+def expected_pairs_decode(seq_lens) -> int:
+    return int(np.maximum(np.asarray(seq_lens, np.int64), 0).sum())
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+__all__ = [
+    "PrefillConfig", "DecodeConfig", "CONFIGS", "normal_f16", "rope_interleaved",
+    "prefill_inputs", "decode_inputs", "paged_layout", "kv_bytes", "PagesLCG",
+    "pages_prefill_case", "pages_decode_case", "paginate", "sample_prefill_rows",
+    "expected_pairs_decode", "ceil_div",
+]

@@ -1,0 +1,149 @@
+"""fp64 CPU oracle for softmax attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and this package imports
+nothing from the product.
+
+It wraps ``liboracle.so`` (``attn_oracle.c``): the plain definition of
+scaled-dot-product attention, ``softmax(Q K^T / sqrt(D) + mask) V``, computed
+in fp64 over the exact values of binary16 inputs.  Prefill follows the
+attention.cuh / test_attention.cu listings of "Tutorial: Adding a New Kernel to
+RL.cu" (layout [B,S,H,D], GQA kv head = h*H_kv//H_q, causal row i sees keys
+0..i); paged decode follows the decode section of the same listing and the
+"KV Cache design" section of the GRPO-CUDA project memory page.
+
+Every function here is pinned by tests in ``tests/test_oracle_pins.py``
+(closed forms, invariants, a library routine on special cases, brute force on
+tiny inputs).  None is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+class Oracle:
+    """ctypes front end of one build of ``attn_oracle.c``.
+
+    The default instance loads ``liboracle.so``; the pin tests also load
+    deliberately broken copies through this class to show that the pins fail.
+    """
+
+    def __init__(self, path: str | None = None):
+        self._path = path
+        self._lib = None
+
+    def _load(self):
+        if self._lib is not None:
+            return self._lib
+        path = self._path
+        if path is None:
+            path = _build.LIB
+            src_mtime = os.path.getmtime(_build.SRC)
+            if not os.path.exists(path) or os.path.getmtime(path) < src_mtime:
+                _build.build()
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        I64 = ctypes.c_int64
+        lib.oracle_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, I64, P]
+        lib.oracle_prefill.restype = I
+        lib.oracle_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I64, P, I64, P]
+        lib.oracle_decode_paged.restype = I
+        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_half_to_double.restype = ctypes.c_double
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = I
+        self._lib = lib
+        return lib
+
+    def num_threads(self) -> int:
+        """OpenMP threads the oracle uses (its ``cores`` figure)."""
+        return self._load().oracle_num_threads()
+
+    def half_to_double(self, bits: int) -> float:
+        """The oracle's own binary16 decoder, exposed for its pin."""
+        return self._load().oracle_half_to_double(int(bits) & 0xFFFF)
+
+    def prefill(self, q, k, v, causal: bool, rows=None, return_lse: bool = False):
+        """fp64 attention for Q [B,S_q,H_q,D], K/V [B,S_kv,H_kv,D] (float16).
+
+        ``rows``: optional int64 flat row ids ``(b*S_q + i)*H_q + h``; the
+        result is then ``[len(rows), D]``, else ``[B,S_q,H_q,D]``.  Returns
+        float64 (and the natural-log LSE per row when ``return_lse``).
+        """
+        q, k, v = _f16(q), _f16(k), _f16(v)
+        B, S_q, H_q, D = q.shape
+        Bk, S_kv, H_kv, Dk = k.shape
+        if v.shape != k.shape or Bk != B or Dk != D:
+            raise ValueError("shape mismatch")
+        if rows is not None:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            n_rows = rows.shape[0]
+            out = np.empty((n_rows, D), np.float64)
+            lse = np.empty(n_rows, np.float64) if return_lse else None
+        else:
+            n_rows = 0
+            out = np.empty((B, S_q, H_q, D), np.float64)
+            lse = np.empty((B, S_q, H_q), np.float64) if return_lse else None
+        rc = self._load().oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv,
+                                         H_q, H_kv, D, int(bool(causal)), _ptr(rows), n_rows,
+                                         _ptr(lse))
+        if rc != 0:
+            raise ValueError(f"oracle_prefill rejected its arguments (rc={rc})")
+        return (out, lse) if return_lse else out
+
+    def decode_paged(self, q, k_cache, v_cache, block_tables, seq_lens, seqs=None,
+                     return_lse: bool = False):
+        """fp64 single-token attention over a paged KV cache.
+
+        q [num_seqs,H_q,D]; caches [num_blocks,H_kv,block_size,D] (float16);
+        block_tables int32 [num_seqs,max_blocks_per_seq]; seq_lens int32
+        [num_seqs].  ``seqs``: optional sequence ids; result
+        ``[len(seqs),H_q,D]`` else ``[num_seqs,H_q,D]``.
+        """
+        q, k_cache, v_cache = _f16(q), _f16(k_cache), _f16(v_cache)
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        num_seqs, H_q, D = q.shape
+        num_blocks, H_kv, block_size, Dk = k_cache.shape
+        if v_cache.shape != k_cache.shape or Dk != D:
+            raise ValueError("shape mismatch")
+        if bt.ndim != 2 or bt.shape[0] != num_seqs or sl.shape != (num_seqs,):
+            raise ValueError("table shape mismatch")
+        if seqs is not None:
+            seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+            n = seqs.shape[0]
+        else:
+            n = num_seqs
+        out = np.empty((n, H_q, D), np.float64)
+        lse = np.empty((n, H_q), np.float64) if return_lse else None
+        rc = self._load().oracle_decode_paged(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(sl), _ptr(out), num_seqs,
+            H_q, H_kv, D, bt.shape[1], block_size, num_blocks, _ptr(seqs),
+            n if seqs is not None else 0, _ptr(lse))
+        if rc != 0:
+            raise ValueError(f"oracle_decode_paged rejected its arguments (rc={rc})")
+        return (out, lse) if return_lse else out
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float16:
+        raise TypeError("oracle inputs are binary16 (numpy float16) arrays")
+    return a
+
+
+default = Oracle()
+num_threads = default.num_threads
+half_to_double = default.half_to_double
+prefill = default.prefill
+decode_paged = default.decode_paged

@@ -1,0 +1,279 @@
+/*
+ * attn_oracle.c -- plain fp64 CPU oracle for scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no code,
+ * header or constant with the HIP library, and the HIP library never calls it.
+ *
+ * What it computes (the plain definition; the pages' online-softmax kernels
+ * reach the same value up to rounding order):
+ *
+ *   For one query row q and its visible key set J:
+ *     s_j  = (sum_d q_d * k_{j,d}) / sqrt(D)                 j in J
+ *     m    = max_j s_j
+ *     P_j  = exp(s_j - m) / sum_{j' in J} exp(s_j' - m)
+ *     o_d  = sum_{j in J} P_j * v_{j,d}
+ *
+ *   Prefill ("Tutorial: Adding a New Kernel to RL.cu", the attention.cuh
+ *   listing, prefill section; and the CPU reference in test_attention.cu):
+ *     Q, K, V laid out [B, S, H, D]; O laid out [B, S_q, H_q, D].
+ *     GQA: H_q % H_kv == 0 and kv head g = (h * H_kv) / H_q (integer division).
+ *     Causal: row i sees keys 0..i; non-causal: all S_kv keys.
+ *
+ *   Paged decode (same page, attention.cuh listing, decode section; and the
+ *   "KV Cache design" section of the GRPO-CUDA project memory page):
+ *     q [num_seqs, H_q, D]; caches [num_blocks, H_kv, block_size, D];
+ *     block_tables [num_seqs, max_blocks_per_seq] maps logical block -> physical;
+ *     seq_lens[s] counts every context token including the new one.
+ *     Token t of sequence s lives at cache[bt[s][t / bs], g, t % bs, :].
+ *     All seq_lens[s] tokens are visible, in logical order.
+ *
+ * Readings taken where the pages are silent (each listed in the design notes):
+ *   - causal with S_q != S_kv is undefined on the pages: rejected (-1).
+ *   - seq_len <= 0 is a precondition violation on the pages; the oracle writes
+ *     a zero row for it, and the same is documented for the GPU path.
+ *   - inputs are IEEE binary16 bit patterns, decoded exactly to fp64 here; the
+ *     scale is 1/sqrt(D) in fp64.
+ *
+ * Every function below works one output row at a time, in the order of the
+ * definition above: gather the visible keys, score them, take the max,
+ * exponentiate, normalise, and sum the weighted value rows.  OpenMP only
+ * distributes independent rows over threads.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- IEEE 754 binary16 -> fp64 (exact) -------------------------------- */
+/* sign(1) | exponent(5, bias 15) | fraction(10).
+ * normal:    (1 + f/1024) * 2^(e-15) = (1024 + f) * 2^(e-25)
+ * subnormal: (f/1024) * 2^-14        = f * 2^-24
+ * e == 31:   infinity (f == 0) or NaN.                                       */
+static double half_bits_to_double(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int e = (h >> 10) & 0x1f;
+  const int f = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
+static double g_h2d[65536];
+static int g_h2d_ready = 0;
+
+static void init_table(void) {
+  if (g_h2d_ready) return;
+  for (int i = 0; i < 65536; ++i) g_h2d[i] = half_bits_to_double((uint16_t)i);
+  g_h2d_ready = 1;
+}
+
+/* Exposed so the tests can check the decoder against an independent one. */
+double oracle_half_to_double(uint16_t h) { return half_bits_to_double(h); }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ---- one softmax-attention row ----------------------------------------- */
+/* q:      D decoded query values
+ * krow/vrow: n pointers to the visible key / value rows (binary16 bits)
+ * scores: scratch of n doubles
+ * out:    D outputs; *lse receives m + log(sum exp(s - m)) (natural log)      */
+static void attend_row(const double* q, const uint16_t* const* krow,
+                       const uint16_t* const* vrow, int64_t n, int D,
+                       double* scores, double* out, double* lse) {
+  if (n <= 0) {
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    if (lse) *lse = -INFINITY;
+    return;
+  }
+  const double scale = 1.0 / sqrt((double)D);
+
+  /* scores s_j = (q . k_j) / sqrt(D) */
+  for (int64_t j = 0; j < n; ++j) {
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += q[d] * g_h2d[krow[j][d]];
+    scores[j] = dot * scale;
+  }
+
+  /* m = max_j s_j */
+  double m = scores[0];
+  for (int64_t j = 1; j < n; ++j)
+    if (scores[j] > m) m = scores[j];
+
+  /* exp(s_j - m) and their sum */
+  double z = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    scores[j] = exp(scores[j] - m);
+    z += scores[j];
+  }
+
+  /* P_j = exp(s_j - m) / z */
+  for (int64_t j = 0; j < n; ++j) scores[j] /= z;
+
+  /* o = sum_j P_j v_j */
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    const double p = scores[j];
+    for (int d = 0; d < D; ++d) out[d] += p * g_h2d[vrow[j][d]];
+  }
+  if (lse) *lse = m + log(z);
+}
+
+/* ---- prefill ----------------------------------------------------------- */
+/* q [B,S_q,H_q,D], k/v [B,S_kv,H_kv,D] binary16 bits, row-major.
+ * rows: optional list of n_rows flat row ids r = (b*S_q + i)*H_q + h; when
+ *       NULL every row is computed and out is [B,S_q,H_q,D] (fp64), else out
+ *       is [n_rows, D] in list order.
+ * lse:  optional, one value per computed row.
+ * Returns 0, or -1 on invalid arguments.                                     */
+int oracle_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   double* out, int B, int S_q, int S_kv, int H_q, int H_kv,
+                   int D, int causal, const int64_t* rows, int64_t n_rows,
+                   double* lse) {
+  if (!q || !k || !v || !out) return -1;
+  if (B <= 0 || S_q <= 0 || S_kv <= 0 || H_q <= 0 || H_kv <= 0 || D <= 0)
+    return -1;
+  if (H_q % H_kv != 0) return -1;
+  if (causal && S_q != S_kv) return -1;
+  init_table();
+
+  const int64_t total = (int64_t)B * S_q * H_q;
+  const int64_t count = rows ? n_rows : total;
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= total) return -1;
+
+  int err = 0;
+#pragma omp parallel
+  {
+    double* qd = (double*)malloc(sizeof(double) * D);
+    double* scores = (double*)malloc(sizeof(double) * (size_t)S_kv);
+    const uint16_t** kr = (const uint16_t**)malloc(sizeof(void*) * (size_t)S_kv);
+    const uint16_t** vr = (const uint16_t**)malloc(sizeof(void*) * (size_t)S_kv);
+    if (!qd || !scores || !kr || !vr) {
+#pragma omp atomic write
+      err = 1;
+    } else {
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t idx = 0; idx < count; ++idx) {
+        const int64_t r = rows ? rows[idx] : idx;
+        const int h = (int)(r % H_q);
+        const int64_t bi = r / H_q;
+        const int i = (int)(bi % S_q);
+        const int b = (int)(bi / S_q);
+        const int g = (int)(((int64_t)h * H_kv) / H_q); /* GQA kv head */
+
+        const uint16_t* qrow = q + (((int64_t)b * S_q + i) * H_q + h) * D;
+        for (int d = 0; d < D; ++d) qd[d] = g_h2d[qrow[d]];
+
+        const int64_t n = causal ? (int64_t)i + 1 : (int64_t)S_kv; /* visible keys */
+        for (int64_t j = 0; j < n; ++j) {
+          const int64_t off = (((int64_t)b * S_kv + j) * H_kv + g) * D;
+          kr[j] = k + off;
+          vr[j] = v + off;
+        }
+        attend_row(qd, kr, vr, n, D, scores, out + idx * D, lse ? lse + idx : NULL);
+      }
+    }
+    free(qd);
+    free(scores);
+    free((void*)kr);
+    free((void*)vr);
+  }
+  return err ? -1 : 0;
+}
+
+/* ---- paged decode ------------------------------------------------------ */
+/* q [num_seqs,H_q,D]; k_cache/v_cache [num_blocks,H_kv,block_size,D];
+ * block_tables int32 [num_seqs,max_blocks_per_seq]; seq_lens int32 [num_seqs].
+ * seqs: optional list of n_seqs sequence ids to compute; out is then
+ *       [n_seqs,H_q,D], else [num_seqs,H_q,D].
+ * Returns 0, -1 on invalid arguments, -2 if a table entry that a visible
+ * token needs is outside [0, num_blocks) or a seq_len exceeds the table.     */
+int oracle_decode_paged(const uint16_t* q, const uint16_t* k_cache,
+                        const uint16_t* v_cache, const int32_t* block_tables,
+                        const int32_t* seq_lens, double* out, int num_seqs,
+                        int H_q, int H_kv, int D, int max_blocks_per_seq,
+                        int block_size, int64_t num_blocks, const int64_t* seqs,
+                        int64_t n_seqs, double* lse) {
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return -1;
+  if (num_seqs <= 0 || H_q <= 0 || H_kv <= 0 || D <= 0 ||
+      max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0)
+    return -1;
+  if (H_q % H_kv != 0) return -1;
+  init_table();
+
+  const int64_t count = seqs ? n_seqs : num_seqs;
+  /* validate everything the rows below will touch */
+  for (int64_t idx = 0; idx < count; ++idx) {
+    const int64_t s = seqs ? seqs[idx] : idx;
+    if (s < 0 || s >= num_seqs) return -1;
+    const int64_t L = seq_lens[s];
+    if (L > (int64_t)max_blocks_per_seq * block_size) return -2;
+    const int64_t nb = L > 0 ? (L + block_size - 1) / block_size : 0;
+    for (int64_t lb = 0; lb < nb; ++lb) {
+      const int32_t phys = block_tables[s * (int64_t)max_blocks_per_seq + lb];
+      if (phys < 0 || phys >= num_blocks) return -2;
+    }
+  }
+
+  int64_t max_len = 1;
+  for (int64_t idx = 0; idx < count; ++idx) {
+    const int64_t s = seqs ? seqs[idx] : idx;
+    if (seq_lens[s] > max_len) max_len = seq_lens[s];
+  }
+
+  int err = 0;
+#pragma omp parallel
+  {
+    double* qd = (double*)malloc(sizeof(double) * D);
+    double* scores = (double*)malloc(sizeof(double) * (size_t)max_len);
+    const uint16_t** kr = (const uint16_t**)malloc(sizeof(void*) * (size_t)max_len);
+    const uint16_t** vr = (const uint16_t**)malloc(sizeof(void*) * (size_t)max_len);
+    if (!qd || !scores || !kr || !vr) {
+#pragma omp atomic write
+      err = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1) collapse(2)
+      for (int64_t idx = 0; idx < count; ++idx) {
+        for (int h = 0; h < H_q; ++h) {
+          const int64_t s = seqs ? seqs[idx] : idx;
+          const int g = (int)(((int64_t)h * H_kv) / H_q); /* GQA kv head */
+          const uint16_t* qrow = q + ((int64_t)s * H_q + h) * D;
+          for (int d = 0; d < D; ++d) qd[d] = g_h2d[qrow[d]];
+
+          const int64_t L = seq_lens[s] > 0 ? seq_lens[s] : 0;
+          for (int64_t t = 0; t < L; ++t) {
+            const int64_t phys =
+                block_tables[s * (int64_t)max_blocks_per_seq + t / block_size];
+            const int64_t off =
+                ((phys * H_kv + g) * (int64_t)block_size + t % block_size) * D;
+            kr[t] = k_cache + off;
+            vr[t] = v_cache + off;
+          }
+          const int64_t o = idx * H_q + h;
+          attend_row(qd, kr, vr, L, D, scores, out + o * D, lse ? lse + o : NULL);
+        }
+      }
+    }
+    free(qd);
+    free(scores);
+    free((void*)kr);
+    free((void*)vr);
+  }
+  return err ? -1 : 0;
+}

@@ -1,0 +1,328 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` takes an oracle object (``oracle.Oracle``) and raises
+``AssertionError`` when the oracle disagrees with the fact.  The pins are run
+against the real oracle (``test_oracle_pins.py``) and against copies with a
+planted mistake (``test_oracle_mutants.py``), which every mistake must trip.
+
+What pins what:
+  * binary16 decoding        -- numpy's own float16 conversion, all 65536 codes
+  * scale 1/sqrt(D), exp sign, normalisation, LSE
+                             -- two-key logistic closed form, D in {32,64,128}
+  * which weight meets which value row
+                             -- three/four-key one-hot closed form
+  * causal extent (j <= i)   -- row 0 equals V[0] exactly; identical keys give
+                                the mean of V[0..i]; future keys are ignored
+  * GQA head mapping (kv head = h*H_kv // H_q, from the attention.cuh listing)
+                             -- per-kv-head constant V
+  * max subtraction (overflow safety)
+                             -- huge logits against torch's fp64 SDPA
+  * everything at once on random data
+                             -- torch.nn.functional.scaled_dot_product_attention
+                                in fp64 on the CPU (library special case)
+  * paging                   -- decode equals the last causal-prefill row,
+                                block-permutation invariance, a brute-force
+                                scipy softmax over the gathered context
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from attention_attn_prefill_amd import workloads as W
+
+
+def _rand16(shape, seed, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float16)
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---- decoding --------------------------------------------------------------
+
+def pin_half_decoder(ora):
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([ora.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "NaN codes decoded differently"
+    assert np.array_equal(got[~nan], ref[~nan]), "binary16 decode differs from numpy"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), "sign of zero"
+
+
+# ---- closed forms ----------------------------------------------------------
+
+def pin_two_key_logistic(ora):
+    """Row 1 of a causal S=2 problem with q1 = 8 e0, k0 = e0, k1 = 0,
+    v0 = e0, v1 = 0 puts weight sigma(8/sqrt(D)) on v0."""
+    for D in (32, 64, 128):
+        q = np.zeros((1, 2, 1, D), np.float16)
+        k = np.zeros_like(q)
+        v = np.zeros_like(q)
+        q[0, 1, 0, 0] = 8.0
+        k[0, 0, 0, 0] = 1.0
+        v[0, 0, 0, 0] = 1.0
+        o, lse = ora.prefill(q, k, v, causal=True, return_lse=True)
+        s0 = 8.0 / math.sqrt(D)
+        want = 1.0 / (1.0 + math.exp(-s0))
+        assert abs(o[0, 1, 0, 0] - want) < 1e-15, (D, o[0, 1, 0, 0], want)
+        assert np.all(o[0, 1, 0, 1:] == 0.0)
+        assert abs(lse[0, 1, 0] - math.log(math.exp(s0) + 1.0)) < 1e-14
+        # the same two keys through the paged decode entry
+        kc = np.zeros((3, 1, 16, D), np.float16)
+        vc = np.zeros_like(kc)
+        kc[2, 0, 0, 0] = 1.0
+        vc[2, 0, 0, 0] = 1.0
+        bt = np.array([[2, -1]], np.int32)
+        od, lsed = ora.decode_paged(q[:, 1], kc, vc, bt, np.array([2], np.int32),
+                                    return_lse=True)
+        assert abs(od[0, 0, 0] - want) < 1e-15, (D, od[0, 0, 0], want)
+        assert np.all(od[0, 0, 1:] == 0.0)
+        assert abs(lsed[0, 0] - math.log(math.exp(s0) + 1.0)) < 1e-14
+    # sigma(8/sqrt(128)) = sigma(0.70711) = 0.66976 to five places
+    q = np.zeros((1, 2, 1, 128), np.float16)
+    k = np.zeros_like(q)
+    v = np.zeros_like(q)
+    q[0, 1, 0, 0], k[0, 0, 0, 0], v[0, 0, 0, 0] = 8.0, 1.0, 1.0
+    assert abs(ora.prefill(q, k, v, True)[0, 1, 0, 0] - 0.66976) < 5e-6
+
+
+def pin_onehot_distribution(ora):
+    """q = c e0, k_j = a_j e0, v_j = e_j: the output's first coordinates are
+    exactly the softmax weights exp(c a_j / sqrt D) / sum, in key order."""
+    D = 16
+    a = [0.5, -1.0, 1.5, 0.25]
+    c = 4.0
+    n = len(a)
+    q = np.zeros((1, 1, 1, D), np.float16)
+    k = np.zeros((1, n, 1, D), np.float16)
+    v = np.zeros((1, n, 1, D), np.float16)
+    q[0, 0, 0, 0] = c
+    for j in range(n):
+        k[0, j, 0, 0] = a[j]
+        v[0, j, 0, j] = 1.0
+    e = [math.exp(c * aj / math.sqrt(D)) for aj in a]
+    want = np.array([x / sum(e) for x in e])
+    o = ora.prefill(q, k, v, causal=False)
+    assert np.allclose(o[0, 0, 0, :n], want, rtol=0, atol=1e-15), (o[0, 0, 0, :n], want)
+    assert np.all(o[0, 0, 0, n:] == 0.0)
+    # causal view of the same keys: row i sees keys 0..i only
+    qc = np.zeros((1, n, 1, D), np.float16)
+    qc[0, :, 0, 0] = c
+    oc = ora.prefill(qc, k, v, causal=True)
+    for i in range(n):
+        ei = e[: i + 1]
+        assert np.allclose(oc[0, i, 0, : i + 1], np.array(ei) / sum(ei), atol=1e-15)
+        assert np.all(oc[0, i, 0, i + 1:] == 0.0)
+
+
+# ---- causal structure --------------------------------------------------------
+
+def pin_single_visible_key(ora):
+    B, S, H_q, H_kv, D = 2, 5, 4, 2, 16
+    q, k, v = _rand16((B, S, H_q, D), 1), _rand16((B, S, H_kv, D), 2), _rand16((B, S, H_kv, D), 3)
+    o = ora.prefill(q, k, v, causal=True)
+    for b in range(B):
+        for h in range(H_q):
+            g = h * H_kv // H_q
+            assert np.array_equal(o[b, 0, h], _f64(v[b, 0, g])), (b, h)
+
+
+def pin_identical_keys_mean(ora):
+    B, S, H, D = 1, 9, 2, 32
+    q = _rand16((B, S, H, D), 4)
+    k = np.repeat(_rand16((B, 1, H, D), 5), S, axis=1)
+    v = _rand16((B, S, H, D), 6)
+    o = ora.prefill(q, k, v, causal=True)
+    vd = _f64(v)
+    for i in range(S):
+        assert np.allclose(o[0, i], vd[0, : i + 1].mean(axis=0), rtol=0, atol=1e-14), i
+    on = ora.prefill(q, k, v, causal=False)
+    assert np.allclose(on[0], np.broadcast_to(vd[0].mean(axis=0), on[0].shape), atol=1e-14)
+
+
+def pin_future_keys_ignored(ora):
+    B, S, H, D = 1, 12, 2, 16
+    q, k, v = _rand16((B, S, H, D), 7), _rand16((B, S, H, D), 8), _rand16((B, S, H, D), 9)
+    o1 = ora.prefill(q, k, v, causal=True)
+    i0 = 5
+    k2, v2 = k.copy(), v.copy()
+    k2[:, i0 + 1:] = _rand16(k2[:, i0 + 1:].shape, 10, 3.0)
+    v2[:, i0 + 1:] = _rand16(v2[:, i0 + 1:].shape, 11, 3.0)
+    o2 = ora.prefill(q, k2, v2, causal=True)
+    assert np.array_equal(o1[:, : i0 + 1], o2[:, : i0 + 1])
+    assert not np.array_equal(o1[:, i0 + 1:], o2[:, i0 + 1:])
+
+
+# ---- heads -------------------------------------------------------------------
+
+def pin_gqa_mapping(ora):
+    for H_q, H_kv in ((6, 3), (8, 2), (4, 4), (4, 1)):
+        B, S, D = 2, 6, 16
+        q, k = _rand16((B, S, H_q, D), 12), _rand16((B, S, H_kv, D), 13)
+        v = np.zeros((B, S, H_kv, D), np.float16)
+        for g in range(H_kv):
+            v[:, :, g, :] = g + 1
+        for causal in (True, False):
+            o = ora.prefill(q, k, v, causal=causal)
+            for h in range(H_q):
+                want = h * H_kv // H_q + 1
+                assert np.allclose(o[:, :, h, :], want, rtol=0, atol=1e-13), (H_q, H_kv, h)
+            # and through decode
+        kc, vc, bt = W.paginate(k, v, np.full(B, S), 16, 1, (1, 2))
+        od = ora.decode_paged(q[:, -1], kc, vc, bt, np.full(B, S, np.int32))
+        for h in range(H_q):
+            assert np.allclose(od[:, h, :], h * H_kv // H_q + 1, atol=1e-13), (H_q, H_kv, h)
+
+
+# ---- algebra -----------------------------------------------------------------
+
+def pin_linearity_in_v(ora):
+    B, S, H, D = 1, 10, 2, 16
+    q, k = _rand16((B, S, H, D), 14), _rand16((B, S, H, D), 15)
+    n = np.random.default_rng(16).integers(-128, 129, size=(B, S, H, D))
+    v = (n / 64.0).astype(np.float16)
+    v2 = (2.0 * (n / 64.0) + 1.0).astype(np.float16)          # exact in binary16
+    assert np.array_equal(_f64(v2), 2.0 * _f64(v) + 1.0)
+    for causal in (True, False):
+        o1 = ora.prefill(q, k, v, causal=causal)
+        o2 = ora.prefill(q, k, v2, causal=causal)
+        assert np.allclose(o2, 2.0 * o1 + 1.0, rtol=0, atol=1e-13)
+
+
+def pin_values_one_gives_one(ora):
+    B, S, H, D = 2, 7, 3, 32
+    q, k = _rand16((B, S, H, D), 17, 2.0), _rand16((B, S, H, D), 18, 2.0)
+    v = np.ones((B, S, H, D), np.float16)
+    for causal in (True, False):
+        o = ora.prefill(q, k, v, causal=causal)
+        assert np.allclose(o, 1.0, rtol=0, atol=1e-14)
+
+
+def pin_noncausal_key_permutation(ora):
+    B, S_q, S_kv, H, D = 1, 3, 11, 2, 16
+    q, k, v = _rand16((B, S_q, H, D), 19), _rand16((B, S_kv, H, D), 20), _rand16((B, S_kv, H, D), 21)
+    perm = np.random.default_rng(22).permutation(S_kv)
+    o1 = ora.prefill(q, k, v, causal=False)
+    o2 = ora.prefill(q, k[:, perm], v[:, perm], causal=False)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-14)
+
+
+# ---- library special case ------------------------------------------------------
+
+def _torch_sdpa(q, k, v, causal):
+    import torch
+    H_q, H_kv = q.shape[2], k.shape[2]
+    tq = torch.from_numpy(_f64(q)).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(_f64(k)).permute(0, 2, 1, 3).repeat_interleave(H_q // H_kv, dim=1)
+    tv = torch.from_numpy(_f64(v)).permute(0, 2, 1, 3).repeat_interleave(H_q // H_kv, dim=1)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    return out.permute(0, 2, 1, 3).contiguous().numpy()
+
+
+def pin_matches_torch_sdpa(ora):
+    cases = [
+        (1, 17, 17, 4, 2, 32, True),
+        (2, 33, 33, 6, 3, 64, True),
+        (2, 9, 21, 4, 1, 128, False),
+        (3, 16, 16, 2, 2, 16, False),
+    ]
+    for i, (B, S_q, S_kv, H_q, H_kv, D, causal) in enumerate(cases):
+        q = _rand16((B, S_q, H_q, D), 30 + i)
+        k = _rand16((B, S_kv, H_kv, D), 40 + i)
+        v = _rand16((B, S_kv, H_kv, D), 50 + i)
+        o = ora.prefill(q, k, v, causal=causal)
+        assert np.allclose(o, _torch_sdpa(q, k, v, causal), rtol=1e-12, atol=1e-13), i
+    # the pages' own first unit-test case (LCG inputs, B=1 S=16 H 2/1)
+    q, k, v = W.pages_prefill_case(W.PagesLCG(42), 1, 16, 2, 1)
+    assert np.allclose(ora.prefill(q, k, v, True), _torch_sdpa(q, k, v, True),
+                       rtol=1e-12, atol=1e-13)
+
+
+def pin_huge_logits(ora):
+    """Logits of several hundred overflow exp() unless the row max is taken
+    out first; torch's fp64 SDPA handles them, so must the oracle."""
+    B, S, H, D = 1, 6, 1, 16
+    q = np.zeros((B, S, H, D), np.float16)
+    k = np.zeros_like(q)
+    q[..., 0] = 60.0
+    k[0, :, 0, 0] = np.array([60.0, 0.0, -60.0, 60.0, 10.0, 59.5])   # logits 15*k: up to 900
+    v = _rand16((B, S, H, D), 60)
+    for causal in (True, False):
+        o = ora.prefill(q, k, v, causal=causal)
+        assert np.all(np.isfinite(o))
+        assert np.allclose(o, _torch_sdpa(q, k, v, causal), rtol=1e-12, atol=1e-13)
+
+
+# ---- paging --------------------------------------------------------------------
+
+def pin_decode_equals_last_causal_row(ora):
+    H_q, H_kv, D, bs = 4, 2, 32, 16
+    lens = [1, 15, 16, 17, 33, 50]
+    T = max(lens)
+    n = len(lens)
+    Q, K, V = _rand16((n, T, H_q, D), 70), _rand16((n, T, H_kv, D), 71), _rand16((n, T, H_kv, D), 72)
+    kc, vc, bt = W.paginate(K, V, lens, bs, 4, (3, 4))
+    q_last = np.stack([Q[s, L - 1] for s, L in enumerate(lens)])
+    od = ora.decode_paged(q_last, kc, vc, bt, np.array(lens, np.int32))
+    for s, L in enumerate(lens):
+        op = ora.prefill(Q[s:s + 1, :L], K[s:s + 1, :L], V[s:s + 1, :L], causal=True)
+        assert np.allclose(od[s], op[0, L - 1], rtol=0, atol=1e-14), (s, L)
+
+
+def pin_decode_block_permutation(ora):
+    H_q, H_kv, D, bs = 2, 1, 16, 16
+    lens = [40, 7, 64]
+    T = max(lens)
+    K, V = _rand16((3, T, H_kv, D), 80), _rand16((3, T, H_kv, D), 81)
+    q = _rand16((3, H_q, D), 82)
+    sl = np.array(lens, np.int32)
+    kc1, vc1, bt1 = W.paginate(K, V, lens, bs, 5, (5, 1))
+    kc2, vc2, bt2 = W.paginate(K, V, lens, bs, 5, (5, 2))
+    assert not np.array_equal(bt1, bt2)
+    assert np.array_equal(ora.decode_paged(q, kc1, vc1, bt1, sl), ora.decode_paged(q, kc2, vc2, bt2, sl))
+
+
+def pin_decode_brute_force(ora):
+    from scipy.special import softmax
+    H_q, H_kv, D, bs = 2, 1, 16, 16
+    lens = [19, 3]
+    T = max(lens)
+    K, V = _rand16((2, T, H_kv, D), 90), _rand16((2, T, H_kv, D), 91)
+    q = _rand16((2, H_q, D), 92)
+    kc, vc, bt = W.paginate(K, V, lens, bs, 2, (6, 1))
+    od = ora.decode_paged(q, kc, vc, bt, np.array(lens, np.int32))
+    for s, L in enumerate(lens):
+        for h in range(H_q):
+            kk, vv = _f64(K[s, :L, 0]), _f64(V[s, :L, 0])
+            p = softmax(kk @ _f64(q[s, h]) / math.sqrt(D))
+            assert np.allclose(od[s, h], p @ vv, rtol=0, atol=1e-14), (s, h)
+
+
+def pin_decode_zero_length_row(ora):
+    q = _rand16((2, 2, 16), 93)
+    kc, vc = _rand16((2, 1, 16, 16), 94), _rand16((2, 1, 16, 16), 95)
+    bt = np.array([[0], [1]], np.int32)
+    od = ora.decode_paged(q, kc, vc, bt, np.array([0, 5], np.int32))
+    assert np.all(od[0] == 0.0)
+    assert np.all(np.isfinite(od[1])) and not np.all(od[1] == 0.0)
+
+
+def pin_rejects_invalid(ora):
+    q, k = _rand16((1, 4, 2, 16), 96), _rand16((1, 5, 2, 16), 97)
+    for bad in (lambda: ora.prefill(q, k, k, causal=True),                   # causal, S_q != S_kv
+                lambda: ora.prefill(_rand16((1, 4, 3, 16), 98), k, k, False),  # 3 % 2 != 0
+                lambda: ora.decode_paged(_rand16((1, 2, 16), 99), _rand16((2, 1, 16, 16), 1),
+                                         _rand16((2, 1, 16, 16), 2), np.array([[5]], np.int32),
+                                         np.array([4], np.int32))):          # table entry out of range
+        try:
+            bad()
+        except ValueError:
+            continue
+        raise AssertionError("invalid arguments were accepted")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,50 @@
+"""Plant one mistake at a time in a copy of the oracle's C source and check
+that at least one pin fails for it: the pins are strong enough to catch a
+dropped term, a wrong sign, a wrong index or a swapped operand.  CPU only;
+every mutant stays within the arrays the original reads."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from oracle_pins import ALL_PINS
+
+MUTANTS = [
+    ("scale 1/D instead of 1/sqrt(D)", "1.0 / sqrt((double)D)", "1.0 / (double)D"),
+    ("exponent sign flipped", "exp(scores[j] - m)", "exp(m - scores[j])"),
+    ("row max not subtracted", "exp(scores[j] - m)", "exp(scores[j])"),
+    ("normalisation dropped", "scores[j] /= z;", "(void)z;"),
+    ("causal window misses the diagonal", "causal ? (int64_t)i + 1", "causal ? (int64_t)i"),
+    ("GQA head as h % H_kv (prefill)", "const int g = (int)(((int64_t)h * H_kv) / H_q); /* GQA kv head */\n\n        const uint16_t* qrow = q + (((int64_t)b",
+     "const int g = (int)(h % H_kv); /* GQA kv head */\n\n        const uint16_t* qrow = q + (((int64_t)b"),
+    ("GQA head as h % H_kv (decode)", "const int g = (int)(((int64_t)h * H_kv) / H_q); /* GQA kv head */\n          const uint16_t* qrow",
+     "const int g = (int)(h % H_kv); /* GQA kv head */\n          const uint16_t* qrow"),
+    ("value rows read from K", "vr[j] = v + off;", "vr[j] = k + off;"),
+    ("decode slot offset shifted", "t % block_size) * D;", "(t + 1) % block_size) * D;"),
+    ("decode value rows read from K cache", "vr[t] = v_cache + off;", "vr[t] = k_cache + off;"),
+    ("binary16 exponent bias off by one", "e - 25", "e - 24"),
+    ("binary16 subnormal scale", "ldexp((double)f, -24)", "ldexp((double)f, -23)"),
+    ("LSE without the max", "*lse = m + log(z);", "*lse = log(z);"),
+    ("score of key 0 skipped in max", "double m = scores[0];", "double m = scores[n - 1];\n  if (n > 1) m = scores[1];"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, desc, old, new):
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique: {old!r}"
+    path_c = tmp_path / "mutant.c"
+    path_c.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", str(lib),
+                    str(path_c), "-lm"], check=True)
+    ora = oracle.Oracle(str(lib))
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(ora)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake: {desc}"
