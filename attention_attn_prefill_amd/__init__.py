@@ -1,0 +1,20 @@
+"""MI355X (gfx950) scaled-dot-product attention: causal GQA prefill and
+paged single-token decode behind the C ABI of libattn.so (include/attn.h).
+
+``binding`` holds the ctypes front end (same names as the C entry points);
+``workloads`` the seeded synthetic inputs.
+"""
+from .binding import (  # noqa: F401
+    ATTN_ERR_INVALID_ARG,
+    ATTN_ERR_LAUNCH,
+    ATTN_ERR_UNSUPPORTED,
+    ATTN_ERR_WORKSPACE,
+    ATTN_OK,
+    AttnError,
+    attn_abi_version,
+    attn_decode_paged,
+    attn_decode_paged_workspace_size,
+    attn_prefill,
+    attn_status_string,
+    load_library,
+)

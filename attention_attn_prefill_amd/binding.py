@@ -1,0 +1,137 @@
+"""Thin ctypes binding of libattn.so (the C ABI in include/attn.h).
+
+Argument marshalling only: tensor shapes become the integer arguments,
+tensor storage becomes device pointers, the stream defaults to torch's current
+stream.  Every step of the computation runs in the library's HIP kernels; this
+module has no fallback and raises if the library cannot be loaded.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_WORKSPACE = 3
+ATTN_ERR_LAUNCH = 4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {attn_status_string(status)} ({status})")
+
+
+def load_library():
+    """Load libattn.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = I
+    lib.attn_status_string.argtypes = [I]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.attn_prefill.restype = I
+    lib.attn_decode_paged_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.attn_decode_paged_workspace_size.restype = SZ
+    lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I64, P, SZ, P]
+    lib.attn_decode_paged.restype = I
+    _lib = lib
+    return lib
+
+
+def attn_abi_version() -> int:
+    return load_library().attn_abi_version()
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_tensor(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device (cuda) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def attn_prefill(q, k, v, o, causal: bool = True, stream=None) -> None:
+    """O = softmax(Q K^T / sqrt(D) + mask) V via ``attn_prefill``.
+
+    q/o: [B, S_q, H_q, D] float16; k/v: [B, S_kv, H_kv, D] float16, all
+    contiguous device tensors.  Enqueued on ``stream`` (default: current).
+    """
+    import torch
+    B, S_q, H_q, D = q.shape
+    S_kv, H_kv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, S_kv, H_kv, D) or tuple(v.shape) != tuple(k.shape) or \
+            tuple(o.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k, v, o")
+    args = [_dev_tensor(x, torch.float16, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    st = load_library().attn_prefill(*args, B, S_q, S_kv, H_q, H_kv, D, int(bool(causal)),
+                                     _stream_handle(stream, q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_prefill")
+
+
+def attn_decode_paged_workspace_size(num_seqs: int, H_q: int, H_kv: int, head_dim: int,
+                                     max_blocks_per_seq: int, block_size: int) -> int:
+    return int(load_library().attn_decode_paged_workspace_size(
+        num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size))
+
+
+def attn_decode_paged(q, k_cache, v_cache, out, block_tables, seq_lens, workspace=None,
+                      stream=None) -> None:
+    """Single-token attention over a paged cache via ``attn_decode_paged``.
+
+    q/out [num_seqs, H_q, D] float16; caches [num_blocks, H_kv, block_size, D]
+    float16; block_tables [num_seqs, max_blocks_per_seq] int32; seq_lens
+    [num_seqs] int32; workspace: a uint8 device tensor of at least
+    ``attn_decode_paged_workspace_size(...)`` bytes (split-K) or None
+    (single pass).
+    """
+    import torch
+    num_seqs, H_q, D = q.shape
+    num_blocks, H_kv, block_size, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, caches, out")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs or \
+            tuple(seq_lens.shape) != (num_seqs,):
+        raise ValueError("block_tables / seq_lens shape mismatch")
+    ptrs = [_dev_tensor(x, torch.float16, n) for x, n in
+            ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out"))]
+    bt = _dev_tensor(block_tables, torch.int32, "block_tables")
+    sl = _dev_tensor(seq_lens, torch.int32, "seq_lens")
+    if workspace is None:
+        ws, ws_bytes = ctypes.c_void_p(None), 0
+    else:
+        ws = _dev_tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    st = load_library().attn_decode_paged(*ptrs, bt, sl, num_seqs, H_q, H_kv, D,
+                                          block_tables.shape[1], block_size, num_blocks,
+                                          ws, ws_bytes, _stream_handle(stream, q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_paged")

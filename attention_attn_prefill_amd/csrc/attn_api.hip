@@ -1,0 +1,154 @@
+// attn_api.hip -- the extern "C" entry points of libattn.so (see
+// include/attn.h): host-side argument validation, then kernel launches on the
+// caller's stream.  No allocation, no synchronisation, no global state.
+#include "../../include/attn.h"
+
+#include <math.h>
+
+#include "attn_internal.h"
+
+#define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Everything attn_decode_paged checks before the workspace (shared with the
+// workspace-size query so both agree on what is valid).
+attn_status_t check_decode_shape(int num_seqs, int H_q, int H_kv, int head_dim,
+                                 int max_blocks_per_seq, int block_size) {
+  if (num_seqs <= 0 || H_q <= 0 || H_kv <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (H_q % H_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != attn::kDecodeHeadDim || block_size != attn::kDecodeBlockSize)
+    return ATTN_ERR_UNSUPPORTED;
+  if (H_q / H_kv > 8) return ATTN_ERR_UNSUPPORTED;
+  // tokens per sequence must fit an int
+  if ((int64_t)max_blocks_per_seq * block_size > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+struct DecodePlan {
+  int split_blocks;
+  int n_split_max;
+  size_t ws_bytes;  // 0 when no merge pass is needed
+};
+
+DecodePlan plan_decode(int num_seqs, int H_q, int H_kv, int max_blocks_per_seq) {
+  DecodePlan p;
+  p.split_blocks = attn::decode_split_blocks(num_seqs, H_kv, max_blocks_per_seq);
+  p.n_split_max = (int)ceil_div64(max_blocks_per_seq, p.split_blocks);
+  if (p.n_split_max <= 1) {
+    p.ws_bytes = 0;
+  } else {
+    const int64_t slots = (int64_t)num_seqs * H_q * p.n_split_max;
+    p.ws_bytes = (size_t)slots * (attn::kDecodeHeadDim + 2) * sizeof(float);
+  }
+  return p;
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_abi_version(void) { return kAbiVersion; }
+
+ATTN_EXPORT const char* attn_status_string(attn_status_t status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
+  }
+  return "ATTN_ERR_UNKNOWN";
+}
+
+ATTN_EXPORT attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o, int B,
+                                       int S_q, int S_kv, int H_q, int H_kv, int head_dim,
+                                       int causal, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || S_q <= 0 || S_kv <= 0 || H_q <= 0 || H_kv <= 0 || head_dim <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (H_q % H_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if (causal && S_q != S_kv) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return ATTN_ERR_INVALID_ARG;
+  // one workgroup per (128 query rows, q head, batch) must fit a 1-D grid
+  if (ceil_div64(S_q, 128) * H_q * B > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+
+  attn::PrefillArgs a;
+  a.q = static_cast<const _Float16*>(q);
+  a.k = static_cast<const _Float16*>(k);
+  a.v = static_cast<const _Float16*>(v);
+  a.o = static_cast<_Float16*>(o);
+  a.B = B;
+  a.S_q = S_q;
+  a.S_kv = S_kv;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.n_qtiles = 0;  // set by the launcher
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  const hipError_t e = attn::launch_prefill(a, head_dim, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_EXPORT size_t attn_decode_paged_workspace_size(int num_seqs, int H_q, int H_kv, int head_dim,
+                                                    int max_blocks_per_seq, int block_size) {
+  if (check_decode_shape(num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size) != ATTN_OK)
+    return 0;
+  return plan_decode(num_seqs, H_q, H_kv, max_blocks_per_seq).ws_bytes;
+}
+
+ATTN_EXPORT attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                            void* out, const int32_t* block_tables,
+                                            const int32_t* seq_lens, int num_seqs, int H_q,
+                                            int H_kv, int head_dim, int max_blocks_per_seq,
+                                            int block_size, int64_t num_blocks, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens) return ATTN_ERR_INVALID_ARG;
+  const attn_status_t st =
+      check_decode_shape(num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size);
+  if (st != ATTN_OK) return st;
+  if (num_blocks <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (workspace && !aligned(workspace, 16)) return ATTN_ERR_INVALID_ARG;
+
+  DecodePlan plan = plan_decode(num_seqs, H_q, H_kv, max_blocks_per_seq);
+  if (workspace == nullptr || plan.ws_bytes == 0) {
+    // single pass: one split covers the whole table width
+    plan.split_blocks = max_blocks_per_seq;
+    plan.n_split_max = 1;
+  } else if (workspace_bytes < plan.ws_bytes) {
+    return ATTN_ERR_WORKSPACE;
+  }
+  if ((int64_t)plan.n_split_max * H_kv * num_seqs > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+
+  attn::DecodeArgs a;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_cache = static_cast<const _Float16*>(k_cache);
+  a.v_cache = static_cast<const _Float16*>(v_cache);
+  a.out = static_cast<_Float16*>(out);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  float* ws = static_cast<float*>(workspace);
+  const int64_t slots = (int64_t)num_seqs * H_q * plan.n_split_max;
+  a.ws_o = plan.n_split_max > 1 ? ws : nullptr;
+  a.ws_ml = plan.n_split_max > 1 ? ws + slots * attn::kDecodeHeadDim : nullptr;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.split_blocks = plan.split_blocks;
+  a.n_split_max = plan.n_split_max;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  const hipError_t e = attn::launch_decode(a, H_q / H_kv, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

@@ -1,0 +1,54 @@
+// attn_internal.h -- shared declarations between the C-ABI front end and the
+// gfx950 kernels of libattn.so.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// log2(e): softmax is evaluated as exp2((s - m) * scale * log2(e)).
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct PrefillArgs {
+  const _Float16* q;
+  const _Float16* k;
+  const _Float16* v;
+  _Float16* o;
+  int B, S_q, S_kv, H_q, H_kv;
+  int n_qtiles;      // ceil(S_q / BLOCK_M)
+  float scale_log2;  // log2(e) / sqrt(D)
+};
+
+struct DecodeArgs {
+  const _Float16* q;
+  const _Float16* k_cache;
+  const _Float16* v_cache;
+  _Float16* out;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* ws_o;   // [num_seqs, H_q, n_split_max, D] partial outputs (unnormalised)
+  float* ws_ml;  // [num_seqs, H_q, n_split_max, 2] partial (max, sum), log2 domain
+  int64_t num_blocks;
+  int num_seqs, H_q, H_kv;
+  int max_blocks_per_seq;
+  int split_blocks;  // KV blocks per split
+  int n_split_max;   // ceil(max_blocks_per_seq / split_blocks)
+  float scale_log2;
+};
+
+// Launchers: enqueue on `stream`, return the launch status.
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool causal, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
+
+// Decode split policy (shared by the workspace-size query and the launch).
+constexpr int kDecodeBlockSize = 16;
+constexpr int kDecodeHeadDim = 128;
+int decode_split_blocks(int num_seqs, int H_kv, int max_blocks_per_seq);
+
+}  // namespace attn

@@ -1,0 +1,283 @@
+// decode_paged.hip -- single-token attention over a paged KV cache, split-K
+// ("flash-decoding") with a log-sum-exp merge, for gfx950.
+//
+// What is computed follows "Tutorial: Adding a New Kernel to RL.cu",
+// attention.cuh / attention.cu decode sections: q [num_seqs,H_q,D], caches
+// [num_blocks,H_kv,16,D], block_tables maps logical to physical blocks,
+// seq_lens counts the context including the new token; token t lives at
+// cache[bt[s][t/16], g, t%16, :].  The pages' kernel runs one thread per
+// (sequence, head) and walks every token serially; the project memory page
+// ("Remaining Gap vs nano-vllm") names split-K flash-decoding as the fix.
+//
+// Design (bandwidth-bound: every visible K and V byte is read exactly once)
+//   * grid (split, kv head g, sequence); a split covers split_blocks
+//     consecutive logical blocks.  All G = H_q/H_kv query heads of kv head g
+//     are served by the same workgroup, so each K/V byte is fetched once;
+//   * inside a workgroup, wavefront w takes blocks w, w+4, ...; a block of
+//     one kv head is a contiguous 4 KB slab per tensor, read as four
+//     1 KB wavefront loads (lane l: token 4i + l/16, dims 8*(l%16)..+7);
+//   * scores: fp16 dot2 products into fp32, reduced over the 16 lanes of a
+//     token with DPP row operations;
+//   * each 16-lane group keeps its own running (max, sum, o[8 dims]) per
+//     query head, so no cross-group exchange happens inside the loop; the 16
+//     group states of a workgroup are merged through LDS at the end;
+//   * the split's (max, sum, unnormalised o) go to the workspace, and a
+//     second kernel merges splits: M = max m_c, L = sum l_c 2^(m_c - M),
+//     O = sum o_c 2^(m_c - M) / L (scores are kept in the log2 domain).
+//     A sequence that fits one split is finished by the first kernel.
+#include "attn_internal.h"
+
+#include <math.h>
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int D = kDecodeHeadDim;     // 128
+constexpr int BS = kDecodeBlockSize;  // 16
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// Sum over the 16 lanes of a DPP row, result in every lane of the row.
+__device__ __forceinline__ float row16_sum(float x) {
+  // quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_ror:4 = 0x124, row_ror:8 = 0x128
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return x;
+}
+
+__device__ __forceinline__ float dot8(const half8_t& a, const half8_t& b) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2_t x = {a[2 * i], a[2 * i + 1]};
+    const half2_t y = {b[2 * i], b[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2(x, y, acc, false);
+  }
+  return acc;
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+  // linear block id -> (split, kv head, sequence), split fastest
+  const int split = blockIdx.x % a.n_split_max;
+  const int g = (blockIdx.x / a.n_split_max) % a.H_kv;
+  const int s = blockIdx.x / (a.n_split_max * a.H_kv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = lane >> 4;  // token slot inside a 4-token wavefront load
+  const int dl = lane & 15;   // this lane's dims: 8*dl .. 8*dl+7
+
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][G][D];
+  __shared__ int sm_bad;
+
+  const int L_raw = a.seq_lens[s];
+  const int cap = a.max_blocks_per_seq * BS;
+  const bool len_bad = L_raw > cap;
+  const int L = len_bad ? cap : L_raw;
+  const int n_split = L > 0 ? (L + a.split_blocks * BS - 1) / (a.split_blocks * BS) : 0;
+  const bool direct = n_split <= 1;  // this workgroup writes the final output
+
+  if (L <= 0) {
+    // zero-length context: an all-zero row, written once
+    if (split == 0) {
+      for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int j = idx / D, d = idx - j * D;
+        a.out[((int64_t)s * a.H_q + g * G + j) * D + d] = (_Float16)0.0f;
+      }
+    }
+    return;
+  }
+  if (split >= n_split) return;  // empty split
+
+  if (tid == 0) sm_bad = len_bad ? 1 : 0;
+  __syncthreads();
+
+  const int blk_begin = split * a.split_blocks;
+  const int blk_end = min(blk_begin + a.split_blocks, (L + BS - 1) / BS);
+
+  half8_t qv[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    qv[j] = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)s * a.H_q + g * G + j) * D + 8 * dl);
+
+  float m[G], lsum[G], o[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[j][d] = 0.0f;
+  }
+
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int64_t head_off = (int64_t)g * BS * D;
+  const int64_t block_stride = (int64_t)a.H_kv * BS * D;
+
+  for (int blk = blk_begin + wave; blk < blk_end; blk += kWaves) {
+    const int phys = bt[blk];
+    if (phys < 0 || (int64_t)phys >= a.num_blocks) {
+      sm_bad = 1;
+      continue;
+    }
+    const _Float16* kb = a.k_cache + (int64_t)phys * block_stride + head_off;
+    const _Float16* vb = a.v_cache + (int64_t)phys * block_stride + head_off;
+    half8_t kr[4], vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(kb + (4 * i + grp) * D + 8 * dl));
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(vb + (4 * i + grp) * D + 8 * dl));
+    }
+    const int tok0 = blk * BS;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float dot = row16_sum(dot8(qv[j], kr[i]));
+        sc[i] = (tok0 + 4 * i + grp < L) ? dot * a.scale_log2 : -INFINITY;
+      }
+      const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      const float m_new = fmaxf(m[j], mx);
+      if (m_new == -INFINITY) continue;  // no visible token for this group yet
+      const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+      lsum[j] = lsum[j] * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+      m[j] = m_new;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        float acc = o[j][d] * alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(p[i], (float)vr[i][d], acc);
+        o[j][d] = acc;
+      }
+    }
+  }
+
+  // merge the four lane groups of each wavefront (lanes l, l^16, l^32, l^48
+  // hold the same dims for different tokens), then the wavefronts via LDS
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float mm = m[j];
+    mm = fmaxf(mm, __shfl_xor(mm, 16));
+    mm = fmaxf(mm, __shfl_xor(mm, 32));
+    const float w = (m[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[j] - mm);
+    float ls = lsum[j] * w;
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      float x = o[j][d] * w;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      o[j][d] = x;
+    }
+    if (grp == 0) {
+      if (dl == 0) {
+        sm_m[wave][j] = mm;
+        sm_l[wave][j] = ls;
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) sm_o[wave][j][8 * dl + d] = o[j][d];
+    }
+  }
+  __syncthreads();
+
+  const bool bad = sm_bad != 0;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int j = idx / D;
+    const int d = idx - j * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) M = fmaxf(M, sm_m[k][j]);
+    float Ls = 0.0f, Os = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const float mk = sm_m[k][j];
+      const float w = (mk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mk - M);
+      Ls = fmaf(sm_l[k][j], w, Ls);
+      Os = fmaf(sm_o[k][j][d], w, Os);
+    }
+    const int h = g * G + j;
+    if (bad) {
+      M = Ls = Os = __builtin_nanf("");
+    }
+    if (direct) {
+      a.out[((int64_t)s * a.H_q + h) * D + d] = (_Float16)(Os / Ls);
+    } else {
+      const int64_t slot = ((int64_t)s * a.H_q + h) * a.n_split_max + split;
+      a.ws_o[slot * D + d] = Os;
+      if (d == 0) {
+        a.ws_ml[slot * 2 + 0] = M;
+        a.ws_ml[slot * 2 + 1] = Ls;
+      }
+    }
+  }
+}
+
+// One workgroup of D threads per (sequence, query head): merge the splits.
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  const int s = blockIdx.x / a.H_q;
+  const int h = blockIdx.x - s * a.H_q;
+  const int d = threadIdx.x;
+  const int L_raw = a.seq_lens[s];
+  const int cap = a.max_blocks_per_seq * BS;
+  const int L = L_raw > cap ? cap : L_raw;
+  const int n_split = L > 0 ? (L + a.split_blocks * BS - 1) / (a.split_blocks * BS) : 0;
+  if (n_split <= 1) return;  // finished by the split kernel
+  const int64_t base = ((int64_t)s * a.H_q + h) * a.n_split_max;
+  float M = -INFINITY;
+  for (int c = 0; c < n_split; ++c) M = fmaxf(M, a.ws_ml[(base + c) * 2]);
+  float Ls = 0.0f, Os = 0.0f;
+  for (int c = 0; c < n_split; ++c) {
+    const float mc = a.ws_ml[(base + c) * 2];
+    const float w = (mc == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mc - M);
+    Ls = fmaf(a.ws_ml[(base + c) * 2 + 1], w, Ls);
+    Os = fmaf(a.ws_o[(base + c) * D + d], w, Os);
+  }
+  a.out[((int64_t)s * a.H_q + h) * D + d] = (_Float16)(Os / Ls);
+}
+
+template <int G>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  DecodeArgs args = a;
+  void* kargs[] = {&args};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<G>),
+                                 dim3((unsigned)((int64_t)a.n_split_max * a.H_kv * a.num_seqs)), dim3(kThreads), kargs, 0, stream);
+  if (e != hipSuccess || a.n_split_max <= 1) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_merge_kernel),
+                         dim3((unsigned)(a.num_seqs * a.H_q)), dim3(D), kargs, 0, stream);
+}
+
+}  // namespace
+
+int decode_split_blocks(int num_seqs, int H_kv, int max_blocks_per_seq) {
+  (void)num_seqs;
+  (void)H_kv;
+  (void)max_blocks_per_seq;
+  return 32;  // 512 tokens per split
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_g<1>(a, stream);
+    case 2: return launch_g<2>(a, stream);
+    case 3: return launch_g<3>(a, stream);
+    case 4: return launch_g<4>(a, stream);
+    case 5: return launch_g<5>(a, stream);
+    case 6: return launch_g<6>(a, stream);
+    case 7: return launch_g<7>(a, stream);
+    case 8: return launch_g<8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn

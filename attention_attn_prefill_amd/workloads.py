@@ -93,7 +93,6 @@ CONFIGS = {
 def normal_f16(shape, seed_words, threads: int = 16) -> np.ndarray:
     """Standard-normal binary16 array, deterministic in ``seed_words``."""
     n = int(np.prod(shape))
-    out32 = np.empty(n, np.float32)
     out16 = np.empty(n, np.float16)
     nchunks = max(1, (n + _CHUNK - 1) // _CHUNK)
     children = np.random.SeedSequence(list(seed_words)).spawn(nchunks)
@@ -101,8 +100,7 @@ def normal_f16(shape, seed_words, threads: int = 16) -> np.ndarray:
     def fill(c):
         lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
         g = np.random.Generator(np.random.PCG64(children[c]))
-        g.standard_normal(hi - lo, dtype=np.float32, out=out32[lo:hi])
-        out16[lo:hi] = out32[lo:hi]
+        out16[lo:hi] = g.standard_normal(hi - lo, dtype=np.float32)
 
     if nchunks == 1:
         fill(0)

@@ -1,0 +1,206 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal GQA prefill (B=4, S=2048, H_q=16, H_kv=8, D=128) plus
+one paged single-token decode (256 sequences, H_q=16, H_kv=8, D=128,
+block_size=16, seq_lens uniform in [128, 4096], permuted block tables) --
+the Qwen3-0.6B-shaped workloads, both entry points of the C ABI, on synthetic
+seeded inputs already resident in HBM.  ``--workload long`` swaps in the
+long-context pair (prefill B=1 S=32768; decode 64 x 32768 tokens).
+
+Prints one JSON line.  ``value`` is prefill TFLOP/s (exact unmasked-pair flop
+count, 4*D per pair); the decode half of the metric (KV GB/s: K and V bytes
+of every visible token) is in ``decode``.  Per-kernel durations come from HIP
+events recorded on the stream the kernels run on.  ``cpu_baseline`` times
+the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", choices=["qwen3", "long"], default="qwen3")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the oracle sample")
+    return p.parse_args()
+
+
+def cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl, target_s):
+    """The fp64 oracle on a bounded random sample of prefill rows and decode
+    sequences, scaled to the metric's units."""
+    import oracle
+    from attention_attn_prefill_amd import workloads as W
+
+    rng = np.random.default_rng(1234)
+    n_rows_total = pcfg.B * pcfg.S_q * pcfg.H_q
+
+    def pairs_of(rows):
+        pos = (rows // pcfg.H_q) % pcfg.S_q
+        return int((pos + 1).sum()) if pcfg.causal else len(rows) * pcfg.S_kv
+
+    # calibrate on a small sample, then size the real one to ~60 % of the budget
+    cal = rng.choice(n_rows_total, size=min(256, n_rows_total), replace=False).astype(np.int64)
+    t = time.perf_counter()
+    oracle.prefill(q, k, v, pcfg.causal, rows=cal)
+    rate = pairs_of(cal) / max(time.perf_counter() - t, 1e-6)
+    avg_pairs = pcfg.pairs / n_rows_total
+    n = int(min(n_rows_total, max(256, 0.6 * target_s * rate / avg_pairs)))
+    rows = np.sort(rng.choice(n_rows_total, size=n, replace=False)).astype(np.int64)
+    t = time.perf_counter()
+    oracle.prefill(q, k, v, pcfg.causal, rows=rows)
+    tp = time.perf_counter() - t
+    flops = 4 * pcfg.D * pairs_of(rows)
+
+    # decode: sequences in random order until ~40 % of the budget is used
+    order = rng.permutation(dcfg.num_seqs).astype(np.int64)
+    picked, spent, kvb = [], 0.0, 0
+    for chunk in np.array_split(order, max(1, dcfg.num_seqs // 8)):
+        t = time.perf_counter()
+        oracle.decode_paged(dq, kc, vc, bt, sl, seqs=chunk)
+        spent += time.perf_counter() - t
+        picked.extend(chunk.tolist())
+        kvb += W.kv_bytes(sl[chunk], dcfg.H_kv, dcfg.D)
+        if spent > 0.4 * target_s:
+            break
+    return {
+        "value": flops / tp / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"prefill: {n} of {n_rows_total} query rows (uniform random, "
+                  f"{pairs_of(rows)} unmasked pairs) in {tp:.2f} s; decode: {len(picked)} of "
+                  f"{dcfg.num_seqs} sequences in {spent:.2f} s",
+        "decode": {"value": kvb / spent / 1e9, "unit": "GB/s"},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_attn_prefill_amd import (attn_decode_paged, attn_decode_paged_workspace_size,
+                                            attn_prefill)
+    from attention_attn_prefill_amd import workloads as W
+
+    pname, dname = ("qwen3_prefill", "paged_decode") if args.workload == "qwen3" else \
+        ("long_prefill", "long_decode")
+    pcfg, dcfg = W.CONFIGS[pname], W.CONFIGS[dname]
+    print(f"[bench] generating {pname} + {dname} inputs", file=sys.stderr, flush=True)
+    q, k, v = W.prefill_inputs(pcfg)
+    dq, kc, vc, bt, sl = W.decode_inputs(dcfg)
+
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    to = torch.empty_like(tq)
+    tdq, tkc, tvc = (torch.from_numpy(x).to(dev) for x in (dq, kc, vc))
+    tbt, tsl = torch.from_numpy(bt).to(dev), torch.from_numpy(sl).to(dev)
+    tout = torch.empty_like(tdq)
+    ws_bytes = attn_decode_paged_workspace_size(dcfg.num_seqs, dcfg.H_q, dcfg.H_kv, dcfg.D,
+                                                dcfg.max_blocks_per_seq, dcfg.block_size)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    print("[bench] inputs resident in HBM", file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        attn_prefill(tq, tk, tv, to, causal=pcfg.causal, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        attn_decode_paged(tdq, tkc, tvc, tout, tbt, tsl, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    flops = pcfg.flops
+    pre_tflops = flops / (pre_ms * 1e-3) / 1e12
+    kvb = W.kv_bytes(sl, dcfg.H_kv, dcfg.D)
+    dec_gbs = kvb / (dec_ms * 1e-3) / 1e9
+
+    line = {
+        "metric": "prefill TFLOP/s + paged-decode KV GB/s (Qwen3-0.6B shapes), % of roofline",
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (fp32 accumulate)",
+        "data": "synthetic, seeded N(0,1) fp16; permuted block tables",
+        "config": {
+            "workload": f"{pname}: causal GQA prefill B={pcfg.B} S={pcfg.S_q} H_q={pcfg.H_q} "
+                        f"H_kv={pcfg.H_kv} D={pcfg.D}; {dname}: paged decode "
+                        f"{dcfg.num_seqs} seqs, H_q={dcfg.H_q} H_kv={dcfg.H_kv} D={dcfg.D} "
+                        f"block_size={dcfg.block_size}, seq_lens U[{dcfg.len_lo},{dcfg.len_hi}]",
+            "prefill_flops": flops,
+            "prefill_dense_equivalent_flops": pcfg.dense_flops,
+            "decode_kv_bytes": kvb,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "prefill_fwd_kernel<128,causal>",
+            "achieved": round(pre_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(pre_tflops / PEAK_FP16_TFLOPS, 4), "traffic": None,
+            "launch_ms": round(pre_ms, 5),
+        },
+        "decode": {
+            "metric": "paged-decode KV GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
+            "launch_ms": round(dec_ms, 5),
+            "roofline": {
+                "bound": "hbm", "kernel": "decode_split_kernel<2> + decode_merge_kernel",
+                "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            },
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl,
+                                            args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * attn.h -- C ABI of libattn.so: scaled-dot-product attention with online
+ * softmax on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, both from "Tutorial: Adding a New Kernel to RL.cu"
+ * (skillsmp.com add-cuda-kernel page), attention.cuh listing:
+ *   - attn_prefill: causal (or non-causal) GQA prefill, the "Flash Attention 2
+ *     -- Prefill" section of that header;
+ *   - attn_decode_paged: single-token decode against a paged KV cache, the
+ *     "Paged Attention -- Decode" section of that header, run as split-K
+ *     flash-decoding (named as the next step in the "Remaining Gap vs
+ *     nano-vllm" section of the GRPO-CUDA project memory page) with a
+ *     log-sum-exp merge.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers (HIP device memory or memory the device can
+ *     address), except where stated.  The caller owns every buffer; the library
+ *     allocates nothing, keeps no state between calls and is reentrant.
+ *   - fp16 tensors are IEEE binary16, dense, row-major, with the layouts given
+ *     below; every fp16 base pointer must be 16-byte aligned, int32 pointers
+ *     4-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
+ *     and the call returns without synchronising.  A non-OK status means
+ *     nothing was enqueued, except ATTN_ERR_LAUNCH (the launch itself failed).
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     argument never touches the GPU.
+ *   - The softmax scale is 1/sqrt(head_dim) (the launch wrappers of the
+ *     attention.cu listing), applied to fp32 dot products; accumulation is
+ *     fp32; outputs are rounded to fp16 with round-to-nearest-even.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status_t {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, H_q % H_kv != 0,
+                               causal with S_q != S_kv, misaligned pointer */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, block_size,
+                               H_q / H_kv ratio outside the supported set */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace non-NULL but smaller than required */
+  ATTN_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch */
+} attn_status_t;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int attn_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_string(attn_status_t status);
+
+/*
+ * Prefill: O = softmax(Q K^T / sqrt(D) + mask) V for every query row.
+ *
+ *   q  [B, S_q,  H_q,  D] fp16      k, v [B, S_kv, H_kv, D] fp16
+ *   o  [B, S_q,  H_q,  D] fp16 (written)
+ *
+ * GQA: H_q % H_kv == 0; query head h reads kv head (h * H_kv) / H_q
+ * (integer division), as the attention.cuh header states.
+ * causal != 0: row i attends to keys 0..i (the header's causal mask); this
+ * requires S_q == S_kv (the pages define causal prefill for one S only).
+ * causal == 0: every row attends to all S_kv keys (cross-attention).
+ * head_dim (D): 32, 64 or 128.  Any B, S_q, S_kv >= 1 (ragged tails are
+ * masked inside the kernel).
+ */
+attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
+                           int B, int S_q, int S_kv, int H_q, int H_kv,
+                           int head_dim, int causal, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_paged needs for split-K decoding of
+ * up to num_seqs sequences with tables max_blocks_per_seq wide.  Returns 0 if
+ * no workspace is needed (every sequence fits one split), and 0 for invalid
+ * or unsupported arguments (attn_decode_paged reports those).
+ */
+size_t attn_decode_paged_workspace_size(int num_seqs, int H_q, int H_kv,
+                                        int head_dim, int max_blocks_per_seq,
+                                        int block_size);
+
+/*
+ * Paged decode: one new query token per sequence attends to its whole cached
+ * context, in logical order, through the block table.
+ *
+ *   q            [num_seqs, H_q, D] fp16
+ *   k_cache      [num_blocks, H_kv, block_size, D] fp16
+ *   v_cache      [num_blocks, H_kv, block_size, D] fp16
+ *   out          [num_seqs, H_q, D] fp16 (written)
+ *   block_tables [num_seqs, max_blocks_per_seq] int32: logical block ->
+ *                physical block; only entries for blocks below
+ *                ceil(seq_lens[s] / block_size) are read
+ *   seq_lens     [num_seqs] int32: context length including the new token
+ *
+ * Token t of sequence s is k_cache[block_tables[s][t / block_size], g,
+ * t % block_size, :] with g = (h * H_kv) / H_q for query head h (the decode
+ * section of the attention.cuh header and the "KV Cache design" section of
+ * the project memory page).  head_dim must be 128 and block_size 16 (the
+ * only specialisation the pages build); H_q / H_kv must be 1..8.
+ *
+ * num_blocks (not in the pages' signature) bounds the table: the kernel
+ * never reads a block outside [0, num_blocks).
+ *
+ * workspace: device memory of at least attn_decode_paged_workspace_size(...)
+ * bytes selects split-K decoding (sequences cut into fixed token chunks
+ * processed in parallel, then merged by log-sum-exp).  NULL selects the
+ * single-pass kernel (one workgroup walks a whole sequence).  Both give the
+ * same result within fp32 rounding.
+ *
+ * Device-side preconditions (not checkable without a synchronisation):
+ *   1 <= seq_lens[s] <= max_blocks_per_seq * block_size and every table entry
+ *   read lies in [0, num_blocks).  A sequence that breaks them gets NaN in all
+ *   of its output rows; seq_lens[s] <= 0 gets an all-zero row.  No
+ *   out-of-bounds access happens in either case.
+ */
+attn_status_t attn_decode_paged(const void* q, const void* k_cache,
+                                const void* v_cache, void* out,
+                                const int32_t* block_tables,
+                                const int32_t* seq_lens, int num_seqs, int H_q,
+                                int H_kv, int head_dim, int max_blocks_per_seq,
+                                int block_size, int64_t num_blocks,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,117 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/attn.h declares, and rejects invalid arguments on the host, before
+any HIP call (so these tests never touch a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_attn_prefill_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, INV, UNS, WS = (binding.ATTN_OK, binding.ATTN_ERR_INVALID_ARG,
+                    binding.ATTN_ERR_UNSUPPORTED, binding.ATTN_ERR_WORKSPACE)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "attn_abi_version", "attn_status_string", "attn_prefill",
+        "attn_decode_paged_workspace_size", "attn_decode_paged"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_declared_symbols_are_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T " in ln})
+    assert exported == declared_functions()
+
+
+def test_status_strings(lib):
+    assert binding.attn_abi_version() == 1
+    names = [binding.attn_status_string(i) for i in range(5)]
+    assert names == ["ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED",
+                     "ATTN_ERR_WORKSPACE", "ATTN_ERR_LAUNCH"]
+    assert binding.attn_status_string(99) == "ATTN_ERR_UNKNOWN"
+
+
+# Fake, 16-byte aligned addresses: validation must fail before they are used.
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+NULL = ctypes.c_void_p(None)
+
+
+def prefill(lib, q=P, k=P, v=P, o=P2, B=1, S_q=64, S_kv=64, H_q=2, H_kv=1, D=128, causal=1):
+    return lib.attn_prefill(q, k, v, o, B, S_q, S_kv, H_q, H_kv, D, causal, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), INV), (dict(k=NULL), INV), (dict(v=NULL), INV), (dict(o=NULL), INV),
+    (dict(B=0), INV), (dict(S_q=0, S_kv=0), INV), (dict(S_kv=-1, causal=0), INV),
+    (dict(H_q=0), INV), (dict(H_kv=0), INV), (dict(H_q=3, H_kv=2), INV),
+    (dict(S_q=64, S_kv=65, causal=1), INV),
+    (dict(D=96), UNS), (dict(D=256), UNS), (dict(D=0), INV),
+    (dict(q=ctypes.c_void_p(0x10008)), INV), (dict(o=ctypes.c_void_p(0x20002)), INV),
+])
+def test_prefill_rejects(lib, kw, want):
+    assert prefill(lib, **kw) == want
+
+
+def decode(lib, q=P, kc=P, vc=P, out=P2, bt=P, sl=P, num_seqs=4, H_q=16, H_kv=8, D=128,
+           max_bps=256, bs=16, num_blocks=100, ws=NULL, ws_bytes=0):
+    return lib.attn_decode_paged(q, kc, vc, out, bt, sl, num_seqs, H_q, H_kv, D, max_bps, bs,
+                                 num_blocks, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), INV), (dict(kc=NULL), INV), (dict(vc=NULL), INV), (dict(out=NULL), INV),
+    (dict(bt=NULL), INV), (dict(sl=NULL), INV),
+    (dict(num_seqs=0), INV), (dict(H_q=12, H_kv=8), INV), (dict(max_bps=0), INV),
+    (dict(num_blocks=0), INV), (dict(D=64), UNS), (dict(bs=32), UNS),
+    (dict(H_q=32, H_kv=2), UNS),
+    (dict(bt=ctypes.c_void_p(0x10002)), INV), (dict(kc=ctypes.c_void_p(0x10004)), INV),
+    (dict(ws=P, ws_bytes=1024), WS),
+    (dict(ws=ctypes.c_void_p(0x10004), ws_bytes=1 << 30), INV),
+])
+def test_decode_rejects(lib, kw, want):
+    assert decode(lib, **kw) == want
+
+
+def test_workspace_size(lib):
+    # 256 sequences, 16 q heads, tables of 256 blocks: 8 splits of 32 blocks,
+    # each split slot holds 128 fp32 outputs + (max, sum)
+    assert binding.attn_decode_paged_workspace_size(256, 16, 8, 128, 256, 16) == \
+        256 * 16 * 8 * (128 + 2) * 4
+    assert binding.attn_decode_paged_workspace_size(64, 16, 8, 128, 2048, 16) == \
+        64 * 16 * 64 * (128 + 2) * 4
+    # one split per sequence: no workspace
+    assert binding.attn_decode_paged_workspace_size(4, 16, 8, 128, 32, 16) == 0
+    # invalid or unsupported shapes report 0
+    assert binding.attn_decode_paged_workspace_size(4, 16, 8, 64, 256, 16) == 0
+    assert binding.attn_decode_paged_workspace_size(0, 16, 8, 128, 256, 16) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        binding.load_library()

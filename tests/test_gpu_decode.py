@@ -1,0 +1,130 @@
+"""Paged-decode parity: the HIP path (split-K and single pass, through the C
+ABI) against the fp64 oracle, plus paging invariants on the GPU output."""
+import numpy as np
+import pytest
+
+import oracle
+from attention_attn_prefill_amd import AttnError, ATTN_ERR_WORKSPACE
+from attention_attn_prefill_amd import workloads as W
+from gpu_helpers import assert_parity, dev, gpu_decode, gpu_prefill, say
+from test_gpu_prefill import pages_cases
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, seed):
+    return W.normal_f16(shape, (98, seed))
+
+
+def _paged_problem(lens, H_q, H_kv, max_bps, seed, D=128):
+    n = len(lens)
+    q = _rand((n, H_q, D), seed)
+    T = max(max(lens), 1)
+    K, V = _rand((n, T, H_kv, D), seed + 1), _rand((n, T, H_kv, D), seed + 2)
+    kc, vc, bt = W.paginate(K, V, lens, 16, max_bps, (seed, 3))
+    return q, kc, vc, bt, np.array(lens, np.int32), K, V
+
+
+def test_pages_unit_cases():
+    """The pages' decode shapes with their LCG inputs and identity tables."""
+    lcg = W.PagesLCG(42)
+    for kind, B, S, H_q, H_kv, D in pages_cases():
+        if kind == "prefill":
+            W.pages_prefill_case(lcg, B, S, H_q, H_kv, D)  # keep the LCG stream in step
+            continue
+        q, kc, vc, bt, sl, _, _ = W.pages_decode_case(lcg, B, S, H_q, H_kv, D)
+        say("pages decode", B, S, H_q, H_kv)
+        ref = oracle.decode_paged(q, kc, vc, bt, sl)
+        for split in (True, False):
+            err = assert_parity(gpu_decode(q, kc, vc, bt, sl, split), ref, "pages decode")
+            assert err < 5e-3
+
+
+def test_paged_decode_full():
+    cfg = W.CONFIGS["paged_decode"]
+    q, kc, vc, bt, sl = W.decode_inputs(cfg)
+    say("paged_decode full", kc.shape)
+    ref = oracle.decode_paged(q, kc, vc, bt, sl)
+    assert_parity(gpu_decode(q, kc, vc, bt, sl, split=True), ref, "paged_decode split")
+    assert_parity(gpu_decode(q, kc, vc, bt, sl, split=False), ref, "paged_decode single")
+
+
+@pytest.mark.timeout(900)
+def test_long_decode_full_size_sampled_seqs():
+    cfg = W.CONFIGS["long_decode"]
+    say("long_decode: generating 2 x 8 GiB of cache")
+    q, kc, vc, bt, sl = W.decode_inputs(cfg)
+    say("long_decode full size", kc.shape)
+    got = gpu_decode(q, kc, vc, bt, sl, split=True)
+    seqs = np.array([0, 17, 41, 63], np.int64)
+    ref = oracle.decode_paged(q, kc, vc, bt, sl, seqs=seqs)
+    assert_parity(got[seqs], ref, "long_decode")
+
+
+LENS = [1, 2, 15, 16, 17, 31, 32, 33, 100, 511, 512, 513, 1000, 1024, 1500, 2049]
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(16, 8), (8, 8), (16, 4), (8, 1), (6, 2), (3, 1)])
+def test_ragged_lengths_and_group_sizes(H_q, H_kv):
+    q, kc, vc, bt, sl, _, _ = _paged_problem(LENS, H_q, H_kv, 160, H_q * 10 + H_kv)
+    say("ragged", H_q, H_kv)
+    ref = oracle.decode_paged(q, kc, vc, bt, sl)
+    split = gpu_decode(q, kc, vc, bt, sl, split=True)
+    single = gpu_decode(q, kc, vc, bt, sl, split=False)
+    assert_parity(split, ref, "split")
+    assert_parity(single, ref, "single")
+
+
+def test_block_permutation_invariance_is_bitwise():
+    lens = [700, 33, 1200, 16]
+    n, H_q, H_kv, D = len(lens), 16, 8, 128
+    q = _rand((n, H_q, D), 71)
+    K, V = _rand((n, max(lens), H_kv, D), 72), _rand((n, max(lens), H_kv, D), 73)
+    sl = np.array(lens, np.int32)
+    kc1, vc1, bt1 = W.paginate(K, V, lens, 16, 80, (7, 1))
+    kc2, vc2, bt2 = W.paginate(K, V, lens, 16, 80, (7, 2))
+    say("permutation")
+    for split in (True, False):
+        assert np.array_equal(gpu_decode(q, kc1, vc1, bt1, sl, split),
+                              gpu_decode(q, kc2, vc2, bt2, sl, split))
+
+
+def test_decode_equals_last_row_of_causal_prefill():
+    lens = [1, 77, 640]
+    H_q, H_kv, D = 16, 8, 128
+    for i, L in enumerate(lens):
+        Q = _rand((1, L, H_q, D), 80 + i)
+        K, V = _rand((1, L, H_kv, D), 90 + i), _rand((1, L, H_kv, D), 100 + i)
+        kc, vc, bt = W.paginate(K, V, [L], 16, 64, (8, i))
+        say("decode vs prefill", L)
+        pre = gpu_prefill(Q, K, V, True)[0, L - 1].astype(np.float64)
+        dec = gpu_decode(Q[:, L - 1], kc, vc, bt, np.array([L], np.int32))[0].astype(np.float64)
+        assert np.allclose(dec, pre, rtol=2e-2, atol=8e-3)
+
+
+def test_zero_length_gives_zero_row_and_bad_inputs_give_nan():
+    lens = [0, 40, 40, 40, 5000]
+    q, kc, vc, bt, sl, _, _ = _paged_problem([1, 40, 40, 40, 1], 4, 2, 80, 120)
+    sl = np.array(lens, np.int32)       # seq 0 empty, seq 4 longer than its table (80 blocks)
+    bt = bt.copy()
+    bt[2, 1] = kc.shape[0]              # seq 2 points past the pool
+    bt[3, 0] = -7                       # seq 3 has a negative entry
+    bt[4, :] = 0
+    ref = oracle.decode_paged(q, kc, vc, bt, sl, seqs=[1])  # only the valid row
+    for split in (True, False):
+        say("edge rows split" if split else "edge rows single")
+        got = gpu_decode(q, kc, vc, bt, sl, split).astype(np.float64)
+        assert np.all(got[0] == 0.0)
+        assert_parity(got[1].astype(np.float16), ref[0], "valid row next to bad ones")
+        assert np.all(np.isnan(got[2])) and np.all(np.isnan(got[3])) and np.all(np.isnan(got[4]))
+
+
+def test_workspace_too_small_is_rejected():
+    import torch
+    from attention_attn_prefill_amd import attn_decode_paged
+    q, kc, vc, bt, sl, _, _ = _paged_problem([600, 700], 16, 8, 64, 130)
+    ws = torch.empty(64, dtype=torch.uint8, device="cuda")
+    out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+    with pytest.raises(AttnError) as e:
+        attn_decode_paged(dev(q), dev(kc), dev(vc), out, dev(bt), dev(sl), workspace=ws)
+    assert e.value.status == ATTN_ERR_WORKSPACE

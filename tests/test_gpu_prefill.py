@@ -1,0 +1,179 @@
+"""Prefill parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs, plus invariants checked on the GPU output itself."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from attention_attn_prefill_amd import workloads as W
+from gpu_helpers import assert_parity, gpu_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_unit_cases.txt")
+
+
+def pages_cases():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.split("#")[0].split()
+        if line:
+            rows.append((line[0], *map(int, line[1:])))
+    return rows
+
+
+def _rand(shape, seed, scale=1.0):
+    return W.normal_f16(shape, (99, seed)) if scale == 1.0 else \
+        (W.normal_f16(shape, (99, seed)).astype(np.float32) * scale).astype(np.float16)
+
+
+@pytest.mark.parametrize("name", ["tiny_causal", "cross_attn_rope"])
+def test_small_configs_full(name):
+    cfg = W.CONFIGS[name]
+    q, k, v = W.prefill_inputs(cfg)
+    say(name, q.shape, k.shape)
+    got = gpu_prefill(q, k, v, cfg.causal)
+    ref = oracle.prefill(q, k, v, cfg.causal)
+    assert_parity(got, ref, name)
+
+
+def test_pages_unit_cases():
+    """The pages' unit-test shapes and LCG inputs; their pass criterion was a
+    max absolute error below 5e-3, and their kernels reached about 1.2e-4."""
+    lcg = W.PagesLCG(42)
+    for kind, B, S, H_q, H_kv, D in pages_cases():
+        if kind != "prefill":
+            continue
+        q, k, v = W.pages_prefill_case(lcg, B, S, H_q, H_kv, D)
+        say("pages prefill", B, S, H_q, H_kv, D)
+        err = assert_parity(gpu_prefill(q, k, v, True), oracle.prefill(q, k, v, True), "pages")
+        assert err < 5e-3
+
+
+EDGE = [
+    # B, S_q, S_kv, H_q, H_kv, D, causal
+    (1, 1, 1, 2, 1, 128, True),
+    (1, 17, 17, 4, 2, 128, True),
+    (2, 63, 63, 2, 2, 128, True),
+    (1, 64, 64, 8, 1, 128, True),
+    (1, 65, 65, 4, 4, 128, True),
+    (1, 127, 127, 2, 1, 128, True),
+    (1, 129, 129, 4, 2, 128, True),
+    (3, 200, 200, 6, 3, 128, True),
+    (1, 257, 257, 2, 1, 64, True),
+    (2, 300, 300, 4, 2, 32, True),
+    (1, 1, 300, 4, 2, 128, False),
+    (2, 33, 100, 4, 1, 128, False),
+    (1, 130, 7, 2, 2, 64, False),
+    (1, 256, 64, 8, 8, 32, False),
+    (1, 384, 384, 2, 1, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,S_q,S_kv,H_q,H_kv,D,causal", EDGE)
+def test_edge_shapes(B, S_q, S_kv, H_q, H_kv, D, causal):
+    seed = hash((B, S_q, S_kv, H_q, H_kv, D, causal)) % 10000
+    q = _rand((B, S_q, H_q, D), seed)
+    k = _rand((B, S_kv, H_kv, D), seed + 1)
+    v = _rand((B, S_kv, H_kv, D), seed + 2)
+    say("edge", B, S_q, S_kv, H_q, H_kv, D, causal)
+    assert_parity(gpu_prefill(q, k, v, causal), oracle.prefill(q, k, v, causal), "edge")
+
+
+def test_large_logits():
+    """Scores of several tens force max updates inside the running softmax."""
+    B, S, H_q, H_kv, D = 1, 320, 4, 2, 128
+    q = _rand((B, S, H_q, D), 11, 3.0)
+    k = _rand((B, S, H_kv, D), 12, 3.0)
+    v = _rand((B, S, H_kv, D), 13)
+    say("large logits")
+    for causal in (True, False):
+        assert_parity(gpu_prefill(q, k, v, causal), oracle.prefill(q, k, v, causal), "large")
+
+
+def test_increasing_logits():
+    """Keys aligned with the query and growing along the sequence: the row
+    max grows in every tile, so every tile rescales the running output."""
+    B, S, H, D = 1, 512, 1, 128
+    rng = np.random.default_rng(5)
+    qhat = rng.standard_normal(D)
+    qhat /= np.linalg.norm(qhat)
+    q = np.broadcast_to((4.0 * qhat).astype(np.float16), (B, S, H, D)).copy()
+    kf = (np.arange(S)[:, None] / S * 6.0) * qhat[None, :] + 0.05 * rng.standard_normal((S, D))
+    k = kf.astype(np.float16).reshape(B, S, H, D)
+    v = _rand((B, S, H, D), 14)
+    say("increasing logits")
+    assert_parity(gpu_prefill(q, k, v, True), oracle.prefill(q, k, v, True), "increasing")
+
+
+def test_qwen3_prefill_full_size_sampled_rows():
+    cfg = W.CONFIGS["qwen3_prefill"]
+    q, k, v = W.prefill_inputs(cfg)
+    say("qwen3_prefill full size")
+    got = gpu_prefill(q, k, v, True).reshape(-1, cfg.D)
+    rows = W.sample_prefill_rows(cfg, 3000)
+    ref = oracle.prefill(q, k, v, True, rows=rows)
+    assert_parity(got[rows], ref, "qwen3_prefill")
+
+
+@pytest.mark.timeout(600)
+def test_long_prefill_full_size_sampled_rows():
+    cfg = W.CONFIGS["long_prefill"]
+    q, k, v = W.prefill_inputs(cfg)
+    say("long_prefill full size")
+    got = gpu_prefill(q, k, v, True).reshape(-1, cfg.D)
+    rows = W.sample_prefill_rows(cfg, 400, tile=4096)
+    ref = oracle.prefill(q, k, v, True, rows=rows)
+    assert_parity(got[rows], ref, "long_prefill")
+
+
+# ---- invariants on the GPU output ------------------------------------------
+
+def test_values_one_give_one():
+    B, S, H_q, H_kv, D = 2, 200, 4, 2, 128
+    q, k = _rand((B, S, H_q, D), 21, 2.0), _rand((B, S, H_kv, D), 22, 2.0)
+    v = np.ones((B, S, H_kv, D), np.float16)
+    for causal in (True, False):
+        got = gpu_prefill(q, k, v, causal).astype(np.float64)
+        assert np.allclose(got, 1.0, rtol=0, atol=ATOL_ONE)
+
+
+ATOL_ONE = 2e-3  # the fp16 weights sum to 1 within rounding
+
+
+def test_row0_is_v0_exactly():
+    B, S, H_q, H_kv, D = 2, 150, 8, 2, 128
+    q, k, v = _rand((B, S, H_q, D), 31), _rand((B, S, H_kv, D), 32), _rand((B, S, H_kv, D), 33)
+    got = gpu_prefill(q, k, v, True)
+    for h in range(H_q):
+        assert np.array_equal(got[:, 0, h], v[:, 0, h * H_kv // H_q])
+
+
+def test_future_keys_do_not_change_past_rows():
+    B, S, H, D = 1, 300, 2, 128
+    q, k, v = _rand((B, S, H, D), 41), _rand((B, S, H, D), 42), _rand((B, S, H, D), 43)
+    o1 = gpu_prefill(q, k, v, True)
+    cut = 137
+    k2, v2 = k.copy(), v.copy()
+    k2[:, cut + 1:] = _rand(k2[:, cut + 1:].shape, 44, 2.0)
+    v2[:, cut + 1:] = _rand(v2[:, cut + 1:].shape, 45, 2.0)
+    o2 = gpu_prefill(q, k2, v2, True)
+    assert np.array_equal(o1[:, : cut + 1], o2[:, : cut + 1])
+
+
+def test_gqa_constant_values():
+    B, S, H_q, H_kv, D = 1, 130, 8, 2, 128
+    q, k = _rand((B, S, H_q, D), 51), _rand((B, S, H_kv, D), 52)
+    v = np.zeros((B, S, H_kv, D), np.float16)
+    for g in range(H_kv):
+        v[:, :, g] = g + 1
+    got = gpu_prefill(q, k, v, True).astype(np.float64)
+    for h in range(H_q):
+        assert np.allclose(got[:, :, h], h * H_kv // H_q + 1, rtol=0, atol=4e-3)
+
+
+def test_deterministic():
+    B, S, H_q, H_kv, D = 1, 333, 4, 2, 128
+    q, k, v = _rand((B, S, H_q, D), 61), _rand((B, S, H_kv, D), 62), _rand((B, S, H_kv, D), 63)
+    assert np.array_equal(gpu_prefill(q, k, v, True), gpu_prefill(q, k, v, True))
