@@ -38,9 +38,43 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=["qwen3", "long"], default="qwen3")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--profile", action="store_true",
+                   help="counter runs: no CPU baseline, and first a plain 512 MiB fp16 "
+                        "negation (reads and writes 512 MiB) to calibrate the byte counters")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle sample")
     return p.parse_args()
+
+
+KERNEL_SOURCES = {
+    "prefill_fwd_kernel": ["attention_attn_prefill_amd/csrc/prefill_fwd.hip",
+                           "attention_attn_prefill_amd/csrc/attn_internal.h"],
+    "decode_split_kernel": ["attention_attn_prefill_amd/csrc/decode_paged.hip",
+                            "attention_attn_prefill_amd/csrc/attn_internal.h"],
+}
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch (read + write) from the committed counter summary
+    profiles/hbm_traffic_<workload>.md, or None when the kernel's source has
+    changed since those counters were taken (or none were taken)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    entry = json.loads(m.group(1))["kernels"].get(kernel)
+    if entry is None:
+        return None
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest()[:16] != entry["source_sha256_16"]:
+        return None
+    return entry["read_bytes"] + entry["write_bytes"]
 
 
 def cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl, target_s):
@@ -122,6 +156,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
     print("[bench] inputs resident in HBM", file=sys.stderr, flush=True)
+    if args.profile:
+        args.no_cpu_baseline = True
+        src = torch.ones(256 << 20, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] calibration copy: 512 MiB read + 512 MiB written", file=sys.stderr, flush=True)
 
     def step(ev=None):
         if ev is not None:
@@ -156,6 +198,8 @@ def main():
     kvb = W.kv_bytes(sl, dcfg.H_kv, dcfg.D)
     dec_gbs = kvb / (dec_ms * 1e-3) / 1e9
 
+    traffic_key = f"{pname}_{dname}"
+    pcfg_bytes = 2 * (q.size + k.size + v.size + q.size)
     line = {
         "metric": "prefill TFLOP/s + paged-decode KV GB/s (Qwen3-0.6B shapes), % of roofline",
         "value": round(pre_tflops, 2),
@@ -182,7 +226,10 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": "prefill_fwd_kernel<128,causal>",
             "achieved": round(pre_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(pre_tflops / PEAK_FP16_TFLOPS, 4), "traffic": None,
+            "frac": round(pre_tflops / PEAK_FP16_TFLOPS, 4),
+            "traffic": measured_traffic(traffic_key, "prefill_fwd_kernel"),
+            "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
+            "algorithmic_bytes": pcfg_bytes,
             "launch_ms": round(pre_ms, 5),
         },
         "decode": {
@@ -191,7 +238,8 @@ def main():
             "roofline": {
                 "bound": "hbm", "kernel": "decode_split_kernel<2> + decode_merge_kernel",
                 "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(traffic_key, "decode_split_kernel"),
             },
         },
     }
