@@ -80,6 +80,8 @@ ATTN_EXPORT attn_status_t attn_prefill(const void* q, const void* k, const void*
     return ATTN_ERR_INVALID_ARG;
   // one workgroup per (128 query rows, q head, batch) must fit a 1-D grid
   if (ceil_div64(S_q, 128) * H_q * B > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  // K/V rows of one batch entry are addressed with 32-bit byte offsets
+  if ((int64_t)S_kv * H_kv * head_dim * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
 
   attn::PrefillArgs a;
   a.q = static_cast<const _Float16*>(q);

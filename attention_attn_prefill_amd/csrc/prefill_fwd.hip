@@ -36,8 +36,9 @@
 //     that actually enter the PV product (v_dot2_f32_f16 against ones);
 //   * causal: tiles strictly above the diagonal are never loaded; only tiles
 //     crossing the diagonal (or the ragged end) are masked element-wise;
-//   * workgroups are issued longest-first (last query tiles first) so the
-//     causal triangle's long tiles do not trail at the end of the grid.
+//   * a workgroup runs query tiles i and n-1-i back to back: under the causal
+//     mask every such pair costs the same, so the grid has no tail of long
+//     tiles (an odd middle tile runs alone, last).
 #include "attn_internal.h"
 
 #include <math.h>
@@ -71,256 +72,375 @@ __device__ __forceinline__ float wave_half_swap_add(float x) {
 // {0,2,1,3}.
 __device__ __forceinline__ int vt_pos_group(int a) { return (a == 1) ? 2 : (a == 2) ? 1 : a; }
 
+// A raw buffer resource over [p, p + bytes).  The base address is passed
+// through readfirstlane so the descriptor lives in SGPRs (it is workgroup-
+// uniform); a VGPR descriptor would turn every load into a waterfall loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const _Float16* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Per-thread staging of the K and V tiles: global -> registers (issued early)
+// -> LDS (written after the math of the current tile).  The K tile is written
+// row-major, the V tile transposed, 4 keys x 8 dims per work item.
+// Loads go through buffer resources whose range is the kv head's rows
+// [0, S_kv): rows past the end read as zeros (and are masked), with no
+// clamping arithmetic and 32-bit offsets.
 template <int D, int HP>
-struct TileStage {
+struct Stager {
   static constexpr int kThreads = 64 * kWavesPerHead * HP;
-  static constexpr int VEC_PER_ROW = D / 8;                              // 16-byte vectors per key row
-  static constexpr int K_VECS = kBlockN * VEC_PER_ROW;                   // K tile vectors
-  static constexpr int V_ITEMS = (kBlockN / 4) * VEC_PER_ROW;           // (4 keys x 8 dims) items
+  static constexpr int VEC_PER_ROW = D / 8;                     // 16-byte vectors per key row
+  static constexpr int K_VECS = kBlockN * VEC_PER_ROW;
+  static constexpr int V_ITEMS = (kBlockN / 4) * VEC_PER_ROW;
   static constexpr int K_PER_T = (K_VECS + kThreads - 1) / kThreads;
   static constexpr int V_PER_T = (V_ITEMS + kThreads - 1) / kThreads;
+  static constexpr int KROW = D + 8;
+  static constexpr int VROW = kBlockN + 8;
+
   half8_t kreg[K_PER_T];
   half8_t vreg[V_PER_T][4];
-};
+  __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+  int row_bytes;  // bytes between consecutive key rows (H_kv * D * 2)
 
-template <int D, int HP>
-__device__ __forceinline__ void stage_load(TileStage<D, HP>& st, const _Float16* kbase,
-                                           const _Float16* vbase, int64_t row_stride, int kv0,
-                                           int S_kv, int tid) {
-  using TS = TileStage<D, HP>;
-  const int last = S_kv - 1;
-#pragma unroll
-  for (int u = 0; u < TS::K_PER_T; ++u) {
-    const int idx = tid + u * TS::kThreads;
-    if (idx < TS::K_VECS) {
-      const int r = idx / TS::VEC_PER_ROW;
-      const int c = idx - r * TS::VEC_PER_ROW;
-      const int key = min(kv0 + r, last);  // rows past the end repeat a valid row; they are masked
-      st.kreg[u] = *reinterpret_cast<const half8_t*>(kbase + (int64_t)key * row_stride + 8 * c);
-    }
+  __device__ __forceinline__ void init(const _Float16* kbase, const _Float16* vbase, int row_stride,
+                                       int S_kv) {
+    row_bytes = row_stride * 2;
+    const int range = S_kv * row_bytes;  // host guarantees < 2^31
+    krsrc = make_rsrc(kbase, range);
+    vrsrc = make_rsrc(vbase, range);
   }
-#pragma unroll
-  for (int u = 0; u < TS::V_PER_T; ++u) {
-    const int idx = tid + u * TS::kThreads;
-    if (idx < TS::V_ITEMS) {
-      const int kg = idx % (kBlockN / 4);
-      const int c = idx / (kBlockN / 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = min(kv0 + 4 * kg + j, last);
-        st.vreg[u][j] = *reinterpret_cast<const half8_t*>(vbase + (int64_t)key * row_stride + 8 * c);
-      }
-    }
-  }
-}
+  __device__ __forceinline__ static bool k_mine(int u, int tid) { return tid + u * kThreads < K_VECS; }
+  __device__ __forceinline__ static bool v_mine(int u, int tid) { return tid + u * kThreads < V_ITEMS; }
 
-template <int D, int HP>
-__device__ __forceinline__ void stage_store(const TileStage<D, HP>& st, _Float16* k_lds,
-                                            _Float16* vt_lds, int tid) {
-  using TS = TileStage<D, HP>;
-  constexpr int KROW = D + 8;
-  constexpr int VROW = kBlockN + 8;
+  __device__ __forceinline__ void load_k(int kv0, int tid) {
 #pragma unroll
-  for (int u = 0; u < TS::K_PER_T; ++u) {
-    const int idx = tid + u * TS::kThreads;
-    if (idx < TS::K_VECS) {
-      const int r = idx / TS::VEC_PER_ROW;
-      const int c = idx - r * TS::VEC_PER_ROW;
-      *reinterpret_cast<half8_t*>(&k_lds[r * KROW + 8 * c]) = st.kreg[u];
+    for (int u = 0; u < K_PER_T; ++u) {
+      if (!k_mine(u, tid)) continue;
+      const int idx = tid + u * kThreads;
+      const int r = idx / VEC_PER_ROW, c = idx % VEC_PER_ROW;
+      const int off = (kv0 + r) * row_bytes + 16 * c;
+      kreg[u] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off, 0, 0));
     }
   }
+  __device__ __forceinline__ void load_v(int kv0, int tid) {
 #pragma unroll
-  for (int u = 0; u < TS::V_PER_T; ++u) {
-    const int idx = tid + u * TS::kThreads;
-    if (idx < TS::V_ITEMS) {
-      const int kg = idx % (kBlockN / 4);
-      const int c = idx / (kBlockN / 4);
-      const int pos = (kg >> 2) * 16 + vt_pos_group(kg & 3) * 4;
+    for (int u = 0; u < V_PER_T; ++u) {
+      if (!v_mine(u, tid)) continue;
+      const int idx = tid + u * kThreads;
+      const int kg = idx % (kBlockN / 4), c = idx / (kBlockN / 4);
+      const int off = (kv0 + 4 * kg) * row_bytes + 16 * c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vreg[u][j] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off + j * row_bytes, 0, 0));
+    }
+  }
+  __device__ __forceinline__ void store_k(_Float16* k_lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < K_PER_T; ++u) {
+      if (!k_mine(u, tid)) continue;
+      const int idx = tid + u * kThreads;
+      const int r = idx / VEC_PER_ROW, c = idx % VEC_PER_ROW;
+      *reinterpret_cast<half8_t*>(&k_lds[r * KROW + 8 * c]) = kreg[u];
+    }
+  }
+  __device__ __forceinline__ void store_v(_Float16* vt_lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < V_PER_T; ++u) {
+      if (!v_mine(u, tid)) continue;
+      const int idx = tid + u * kThreads;
+      const int kg = idx % (kBlockN / 4), c = idx / (kBlockN / 4);
+      const int base = (8 * c) * VROW + (kg >> 2) * 16 + vt_pos_group(kg & 3) * 4;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        half4_t col4 = {st.vreg[u][0][i], st.vreg[u][1][i], st.vreg[u][2][i], st.vreg[u][3][i]};
-        *reinterpret_cast<half4_t*>(&vt_lds[(8 * c + i) * VROW + pos]) = col4;
+        half4_t col4 = {vreg[u][0][i], vreg[u][1][i], vreg[u][2][i], vreg[u][3][i]};
+        *reinterpret_cast<half4_t*>(&vt_lds[base + i * VROW]) = col4;
       }
     }
   }
+};
+
+// S^T tile (64 keys x 32 queries) = K_tile . Q_w^T from an LDS K buffer.
+// The two 32-key accumulators alternate so consecutive MFMAs are
+// independent, and operand reads run four MFMAs ahead of their use.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16_t (&s)[2], const _Float16* kl, const half8_t (&qf)[D / 16]) {
+  constexpr int KROW = D + 8;
+  constexpr int N = 2 * (D / 16);
+  constexpr int R = 4;
+  half8_t ring[R];
+  s[0] = f32x16_t{};
+  s[1] = f32x16_t{};
+#pragma unroll
+  for (int n = 0; n < R; ++n) ring[n] = *reinterpret_cast<const half8_t*>(&kl[(n & 1) * 32 * KROW + 16 * (n >> 1)]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int kb = n & 1, ks = n >> 1;
+    const half8_t kf = ring[n % R];
+    if (n + R < N)
+      ring[n % R] = *reinterpret_cast<const half8_t*>(&kl[((n + R) & 1) * 32 * KROW + 16 * ((n + R) >> 1)]);
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
+  }
 }
 
+// All per-wavefront state of one prefill workgroup, and the per-tile step.
 template <int D, bool CAUSAL, int HP>
-__global__ __launch_bounds__(64 * kWavesPerHead * HP, 2) void prefill_fwd_kernel(PrefillArgs a) {
-  constexpr int kThreads = 64 * kWavesPerHead * HP;
-  constexpr int KS = D / 16;           // k-steps of the QK^T contraction
-  constexpr int DT = D / 32;           // 32-wide d tiles of O^T
-  constexpr int KROW = D + 8;          // LDS row stride of K (halfs)
-  constexpr int VROW = kBlockN + 8;    // LDS row stride of V^T (halfs)
-  constexpr int K_LDS = kBlockN * KROW;
-  constexpr int V_LDS = D * VROW;
+struct Prefill {
+  static constexpr int KS = D / 16;         // k-steps of the QK^T contraction
+  static constexpr int DT = D / 32;         // 32-wide d tiles of O^T
+  static constexpr int KROW = D + 8;        // LDS row stride of K (halfs)
+  static constexpr int VROW = kBlockN + 8;  // LDS row stride of V^T (halfs)
+  static constexpr int K_LDS = kBlockN * KROW;
+  static constexpr int V_LDS = D * VROW;
 
-  __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][K_LDS];
-  __shared__ __attribute__((aligned(16))) _Float16 vt_lds[2][V_LDS];
+  _Float16* k_lds;
+  _Float16* vt_lds;
+  const _Float16* kbase;
+  const _Float16* vbase;
+  int64_t kv_row_stride;
+  int S_kv, n_tiles, tid, qw, qrow, hf, k_lane, v_lane;
+  float c2, lazy_raw;
+  Stager<D, HP> st;
+  half8_t qf[KS];
+  f32x16_t o[DT];
+  float m, l;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Stage the next tiles: K runs one tile ahead of V (the math of step t
+  // reads K(t+1) for the next scores and V(t) for this tile's PV product).
+  __device__ __forceinline__ void issue_loads(int t) {
+    if (t + 2 < n_tiles) st.load_k((t + 2) * kBlockN, tid);
+    if (t + 1 < n_tiles) st.load_v((t + 1) * kBlockN, tid);
+  }
+  __device__ __forceinline__ void commit_loads(int t) {
+    if (t + 2 < n_tiles) st.store_k(k_lds + (t & 1) * K_LDS, tid);
+    if (t + 1 < n_tiles) st.store_v(vt_lds + ((t + 1) & 1) * V_LDS, tid);
+    __syncthreads();
+  }
+
+  __device__ __forceinline__ void qk(f32x16_t (&s)[2], int t) const {
+    qk_tile<D>(s, k_lds + (t & 1) * K_LDS + k_lane, qf);
+  }
+
+  // Softmax of tile t's scores and its PV product; when NEXT, the scores of
+  // tile t+1 are computed in the same basic block so that the scheduler can
+  // interleave those MFMAs with this tile's exponentials.
+  template <bool NEXT>
+  __device__ __forceinline__ void step(int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    issue_loads(t);
+    const int kv0 = t * kBlockN;
+    // element-wise mask only where the tile crosses the diagonal or the end
+    const bool need_mask = (CAUSAL && kv0 + kBlockN - 1 > qw) || (kv0 + kBlockN > S_kv);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+          const bool masked = (CAUSAL && key > qrow) || key >= S_kv;
+          if (masked) sc[kb][r] = -INFINITY;
+        }
+      }
+    }
+    // tile max of this query over both lane halves
+    float mx = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[0][r], sc[0][r + 1]));
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[1][r], sc[1][r + 1]));
+    mx = wave_half_swap_max(mx);
+    // move the reference point only when some row's weights would pass 2^8
+    if (__builtin_amdgcn_ballot_w64(mx > m + lazy_raw) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - m_new) * c2);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    const float mb = m * c2;
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+    if (NEXT) qk(sn, t + 1);
+
+    half8_t pf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pf[c][i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[c >> 1][8 * (c & 1) + i], c2, -mb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t pp = {pf[c][2 * i], pf[c][2 * i + 1]};
+        l = __builtin_amdgcn_fdot2(pp, ones, l, false);
+      }
+    }
+    // O^T += V^T P^T, the DT accumulators alternating, reads four ahead
+    const _Float16* vl = vt_lds + (t & 1) * V_LDS + v_lane;
+    {
+      constexpr int N = DT * 4;
+      constexpr int R = 4;
+      half8_t ring[R];
+#pragma unroll
+      for (int n = 0; n < R; ++n) ring[n] = *reinterpret_cast<const half8_t*>(&vl[(n % DT) * 32 * VROW + 16 * (n / DT)]);
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const int dt = n % DT, c = n / DT;
+        const half8_t vf = ring[n % R];
+        if (n + R < N)
+          ring[n % R] = *reinterpret_cast<const half8_t*>(&vl[((n + R) % DT) * 32 * VROW + 16 * ((n + R) / DT)]);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], o[dt], 0, 0, 0);
+      }
+    }
+    commit_loads(t);
+  }
+
+  // a tile this wavefront does not compute (above its diagonal): staging only
+  __device__ __forceinline__ void idle_step(int t) {
+    issue_loads(t);
+    commit_loads(t);
+  }
+};
+
+// One query tile (128 rows of each of the HP heads of head group hg, batch b)
+// against its keys, from the first K/V tile to the last.
+template <int D, bool CAUSAL, int HP>
+__device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int hg, int b,
+                                              _Float16* k_lds, _Float16* vt_lds) {
+
+  using P = Prefill<D, CAUSAL, HP>;
+
+  P p;
+  p.k_lds = k_lds;
+  p.vt_lds = vt_lds;
+  p.tid = threadIdx.x;
+  const int lane = p.tid & 63;
+  const int wave = p.tid >> 6;
   const int col = lane & 31;  // query column of S^T / O^T owned by this lane
-  const int hf = lane >> 5;   // which half of the k-range this lane supplies
+  p.hf = lane >> 5;           // which half of the k-range this lane supplies
 
-  // Longest-first issue order: the slowest-varying part of the linear block
-  // id is the query tile, counted from the end.
-  const int head_groups = a.H_q / HP;
-  const int combos = head_groups * a.B;
-  const int id = blockIdx.x;
-  const int qt = a.n_qtiles - 1 - id / combos;
-  const int rem = id - (id / combos) * combos;
-  const int hg = rem % head_groups;
-  const int b = rem / head_groups;
   const int h = hg * HP + wave / kWavesPerHead;
   const int g = (int)(((int64_t)hg * HP * a.H_kv) / a.H_q);  // shared by the HP heads
 
   const int q0 = qt * kBlockM;
-  const int qw = q0 + (wave % kWavesPerHead) * kRowsPerWave;  // first row of this wavefront
-  const int qrow = qw + col;                                  // this lane's query row
+  p.qw = q0 + (wave % kWavesPerHead) * kRowsPerWave;  // first row of this wavefront
+  p.qrow = p.qw + col;                                // this lane's query row
   const int64_t q_row_stride = (int64_t)a.H_q * D;
-  const int64_t kv_row_stride = (int64_t)a.H_kv * D;
+  p.kv_row_stride = (int64_t)a.H_kv * D;
+  p.S_kv = a.S_kv;
 
   // Q fragment (B operand of S^T = K Q^T): q[qrow][16*ks + 8*hf + 0..7]
-  half8_t qf[KS];
-  if (qrow < a.S_q) {
-    const _Float16* qp = a.q + ((int64_t)b * a.S_q + qrow) * q_row_stride + (int64_t)h * D + 8 * hf;
+  if (p.qrow < a.S_q) {
+    const _Float16* qp = a.q + ((int64_t)b * a.S_q + p.qrow) * q_row_stride + (int64_t)h * D + 8 * p.hf;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const half8_t*>(qp + 16 * ks);
+    for (int ks = 0; ks < P::KS; ++ks) p.qf[ks] = *reinterpret_cast<const half8_t*>(qp + 16 * ks);
   } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = half8_t{};
+    for (int ks = 0; ks < P::KS; ++ks) p.qf[ks] = half8_t{};
   }
-
-  f32x16_t o[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
-  float m = -INFINITY;  // reference point of the exponentials (raw dot-product units)
-  float l = 0.0f;       // this lane's share of the sum of fp16 weights
-  const float c2 = a.scale_log2;
-  const float lazy_raw = kLazyLog2 / c2;
-  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  for (int dt = 0; dt < P::DT; ++dt) p.o[dt] = f32x16_t{};
+  p.m = -INFINITY;  // reference point of the exponentials (raw dot-product units)
+  p.l = 0.0f;       // this lane's share of the sum of fp16 weights
+  p.c2 = a.scale_log2;
+  p.lazy_raw = kLazyLog2 / p.c2;
 
   int n_tiles = (a.S_kv + kBlockN - 1) / kBlockN;
   if (CAUSAL) {
     const int last_row = min(q0 + kBlockM, a.S_q) - 1;
     n_tiles = min(n_tiles, last_row / kBlockN + 1);
   }
-  const int wave_last_row = min(qw + kRowsPerWave - 1, a.S_q - 1);
+  p.n_tiles = n_tiles;
+  const int wave_last_row = min(p.qw + kRowsPerWave - 1, a.S_q - 1);
+  // tiles this wavefront computes: [0, wave_tiles)
+  int wave_tiles = p.qw < a.S_q ? n_tiles : 0;
+  if (CAUSAL) wave_tiles = min(wave_tiles, wave_last_row / kBlockN + 1);
 
-  const _Float16* kbase = a.k + (int64_t)b * a.S_kv * kv_row_stride + (int64_t)g * D;
-  const _Float16* vbase = a.v + (int64_t)b * a.S_kv * kv_row_stride + (int64_t)g * D;
+  p.kbase = a.k + (int64_t)b * a.S_kv * p.kv_row_stride + (int64_t)g * D;
+  p.vbase = a.v + (int64_t)b * a.S_kv * p.kv_row_stride + (int64_t)g * D;
+  p.k_lane = col * P::KROW + 8 * p.hf;
+  p.v_lane = col * P::VROW + 8 * p.hf;
 
-  TileStage<D, HP> st;
-  stage_load<D, HP>(st, kbase, vbase, kv_row_stride, 0, a.S_kv, tid);
-  stage_store<D, HP>(st, k_lds[0], vt_lds[0], tid);
+  // prologue: K(0), V(0) and K(1) into LDS
+  p.st.init(p.kbase, p.vbase, (int)p.kv_row_stride, a.S_kv);
+  p.st.load_k(0, p.tid);
+  p.st.load_v(0, p.tid);
+  p.st.store_k(k_lds, p.tid);
+  p.st.store_v(vt_lds, p.tid);
+  if (n_tiles > 1) {
+    p.st.load_k(kBlockN, p.tid);
+    p.st.store_k(k_lds + P::K_LDS, p.tid);
+  }
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = t * kBlockN;
-    const int buf = t & 1;
-    const bool has_next = t + 1 < n_tiles;
-    if (has_next) stage_load<D, HP>(st, kbase, vbase, kv_row_stride, kv0 + kBlockN, a.S_kv, tid);
-
-    const bool active = qw < a.S_q && !(CAUSAL && kv0 > wave_last_row);
-    if (active) {
-      const _Float16* kl = k_lds[buf];
-      const _Float16* vl = vt_lds[buf];
-      // S^T = K Q^T for the two 32-key halves of the tile
-      f32x16_t s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const half8_t kf = *reinterpret_cast<const half8_t*>(&kl[(kb * 32 + col) * KROW + 16 * ks + 8 * hf]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
-        }
-      }
-
-      // element-wise mask only where the tile crosses the diagonal or the end
-      const bool need_mask = (CAUSAL && kv0 + kBlockN - 1 > qw) || (kv0 + kBlockN > a.S_kv);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-            const bool masked = (CAUSAL && key > qrow) || key >= a.S_kv;
-            if (masked) s[kb][r] = -INFINITY;
-          }
-        }
-      }
-
-      // tile max of this query over both lane halves
-      float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-      for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
-      mx = wave_half_swap_max(mx);
-
-      // move the reference point only when some row's weights would pass 2^8
-      if (__builtin_amdgcn_ballot_w64(mx > m + lazy_raw) != 0) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - m_new) * c2);
-        m = m_new;
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-      }
-      const float mb = m * c2;
-
-      half8_t pf[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          pf[c][i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + i], c2, -mb));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const half2_t pp = {pf[c][2 * i], pf[c][2 * i + 1]};
-          l = __builtin_amdgcn_fdot2(pp, ones, l, false);
-        }
-      }
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const half8_t vf = *reinterpret_cast<const half8_t*>(&vl[(dt * 32 + col) * VROW + 16 * c + 8 * hf]);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], o[dt], 0, 0, 0);
-        }
-      }
-    }
-
-    if (has_next) stage_store<D, HP>(st, k_lds[buf ^ 1], vt_lds[buf ^ 1], tid);
-    __syncthreads();
+  // Every wavefront takes part in all n_tiles staging steps (and barriers);
+  // it computes tiles [0, wave_tiles).  Pairs of steps swap the two score
+  // buffers so no copy is needed.
+  f32x16_t sa[2], sb[2];
+  if (wave_tiles > 0) p.qk(sa, 0);
+  int t = 0;
+  for (; t + 2 < wave_tiles; t += 2) {
+    p.template step<true>(t, sa, sb);
+    p.template step<true>(t + 1, sb, sa);
   }
+  if (t + 1 < wave_tiles) {
+    p.template step<true>(t, sa, sb);
+    p.template step<false>(t + 1, sb, sa);
+    t += 2;
+  } else if (t < wave_tiles) {
+    p.template step<false>(t, sa, sb);
+    t += 1;
+  }
+  for (; t < n_tiles; ++t) p.idle_step(t);
 
   // epilogue: combine the two half-row sums, normalise, round to fp16
-  if (qw >= a.S_q) return;
-  l = wave_half_swap_add(l);
-  if (qrow >= a.S_q) return;
-  const float inv = 1.0f / l;
-  _Float16* op = a.o + ((int64_t)b * a.S_q + qrow) * q_row_stride + (int64_t)h * D;
+  if (p.qw >= a.S_q) return;
+  const float lsum = wave_half_swap_add(p.l);
+  if (p.qrow >= a.S_q) return;
+  const float inv = 1.0f / lsum;
+  _Float16* op = a.o + ((int64_t)b * a.S_q + p.qrow) * q_row_stride + (int64_t)h * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+  for (int dt = 0; dt < P::DT; ++dt) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       half4_t out;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[j] = (_Float16)(o[dt][rg * 4 + j] * inv);
-      *reinterpret_cast<half4_t*>(op + dt * 32 + rg * 8 + hf * 4) = out;
+      for (int j = 0; j < 4; ++j) out[j] = (_Float16)(p.o[dt][rg * 4 + j] * inv);
+      *reinterpret_cast<half4_t*>(op + dt * 32 + rg * 8 + p.hf * 4) = out;
     }
+  }
+}
+
+// Work unit of a workgroup: query tiles qt and n_qtiles-1-qt of one (head
+// group, batch).  Under the causal mask tile i costs i+1 units of 128 keys,
+// so every pair costs the same n_qtiles+1 units and the grid has no
+// long-tile tail; an odd middle tile runs alone, after all pairs.
+template <int D, bool CAUSAL, int HP>
+__global__ __launch_bounds__(64 * kWavesPerHead * HP, 2) void prefill_fwd_kernel(PrefillArgs a) {
+  using P = Prefill<D, CAUSAL, HP>;
+  // K runs one tile ahead of V: at step t the math reads K(t+1) and V(t)
+  __shared__ __attribute__((aligned(16))) _Float16 k_lds[2 * P::K_LDS];
+  __shared__ __attribute__((aligned(16))) _Float16 vt_lds[2 * P::V_LDS];
+
+  const int head_groups = a.H_q / HP;
+  const int combos = head_groups * a.B;
+  const int id = blockIdx.x;
+  const int pair = id / combos;
+  const int rem = id - pair * combos;
+  const int hg = rem % head_groups;
+  const int b = rem / head_groups;
+  const int lo = pair, hi = a.n_qtiles - 1 - pair;
+  prefill_qtile<D, CAUSAL, HP>(a, hi, hg, b, k_lds, vt_lds);
+  if (lo < hi) {
+    __syncthreads();  // the first tile's last LDS reads are done
+    prefill_qtile<D, CAUSAL, HP>(a, lo, hg, b, k_lds, vt_lds);
   }
 }
 
 template <int D, bool CAUSAL, int HP>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.n_qtiles * (a.H_q / HP) * a.B;
+  const int64_t blocks = (int64_t)((a.n_qtiles + 1) / 2) * (a.H_q / HP) * a.B;
   PrefillArgs args = a;
   void* kargs[] = {&args};
   return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_fwd_kernel<D, CAUSAL, HP>),

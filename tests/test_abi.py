@@ -70,6 +70,7 @@ def prefill(lib, q=P, k=P, v=P, o=P2, B=1, S_q=64, S_kv=64, H_q=2, H_kv=1, D=128
     (dict(H_q=0), INV), (dict(H_kv=0), INV), (dict(H_q=3, H_kv=2), INV),
     (dict(S_q=64, S_kv=65, causal=1), INV),
     (dict(D=96), UNS), (dict(D=256), UNS), (dict(D=0), INV),
+    (dict(S_q=1, S_kv=1 << 20, H_q=8, H_kv=8, causal=0), UNS),   # K of one batch entry >= 2 GiB
     (dict(q=ctypes.c_void_p(0x10008)), INV), (dict(o=ctypes.c_void_p(0x20002)), INV),
 ])
 def test_prefill_rejects(lib, kw, want):
