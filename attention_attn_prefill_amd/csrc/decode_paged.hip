@@ -10,17 +10,23 @@
 // ("Remaining Gap vs nano-vllm") names split-K flash-decoding as the fix.
 //
 // Design (bandwidth-bound: every visible K and V byte is read exactly once)
-//   * grid (split, kv head g, sequence); a split covers split_blocks
-//     consecutive logical blocks.  All G = H_q/H_kv query heads of kv head g
+//   * grid (kv head g, sequence, split) with the split index slowest, so the
+//     round-robin deal of workgroups to the 8 XCDs is balanced; a split covers
+//     split_blocks consecutive logical blocks (16..128, the largest that still
+//     leaves 8 workgroups per CU).  All G = H_q/H_kv query heads of kv head g
 //     are served by the same workgroup, so each K/V byte is fetched once;
 //   * inside a workgroup, wavefront w takes blocks w, w+4, ...; a block of
 //     one kv head is a contiguous 4 KB slab per tensor, read as four
-//     1 KB wavefront loads (lane l: token 4i + l/16, dims 8*(l%16)..+7);
+//     1 KB wavefront loads (lane l: token 4i + l/16, dims 8*(l%16)..+7).
+//     The next block's slab is in flight while the current one is reduced,
+//     and table entries arrive 64 at a time (one per lane, broadcast with
+//     readlane);
 //   * scores: fp16 dot2 products into fp32, reduced over the 16 lanes of a
 //     token with DPP row operations;
 //   * each 16-lane group keeps its own running (max, sum, o[8 dims]) per
-//     query head, so no cross-group exchange happens inside the loop; the 16
-//     group states of a workgroup are merged through LDS at the end;
+//     query head, so no cross-group exchange happens inside the loop; at the
+//     end the four groups of a wavefront merge with lane shuffles and the
+//     four wavefronts through LDS;
 //   * the split's (max, sum, unnormalised o) go to the workspace, and a
 //     second kernel merges splits: M = max m_c, L = sum l_c 2^(m_c - M),
 //     O = sum o_c 2^(m_c - M) / L (scores are kept in the log2 domain).
@@ -62,10 +68,15 @@ __device__ __forceinline__ float dot8(const half8_t& a, const half8_t& b) {
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-  // linear block id -> (split, kv head, sequence), split fastest
-  const int split = blockIdx.x % a.n_split_max;
-  const int g = (blockIdx.x / a.n_split_max) % a.H_kv;
-  const int s = blockIdx.x / (a.n_split_max * a.H_kv);
+  // linear block id -> (kv head, sequence, split), split slowest: consecutive
+  // workgroups (which the dispatcher deals round-robin to the 8 XCDs) are
+  // different (sequence, head) pairs of the same split, so every XCD gets an
+  // even share of full splits, and the partial or empty last splits of short
+  // sequences come at the end of the grid.
+  const int pairs = a.num_seqs * a.H_kv;
+  const int split = blockIdx.x / pairs;
+  const int g = (blockIdx.x - split * pairs) % a.H_kv;
+  const int s = (blockIdx.x - split * pairs) / a.H_kv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -117,31 +128,45 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
 
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int64_t head_off = (int64_t)g * BS * D;
   const int64_t block_stride = (int64_t)a.H_kv * BS * D;
+  // this lane's element offset inside a (block, kv head) slab
+  const int64_t lane_off = (int64_t)g * BS * D + grp * D + 8 * dl;
 
-  for (int blk = blk_begin + wave; blk < blk_end; blk += kWaves) {
-    const int phys = bt[blk];
+  // Blocks of this wavefront: blk_begin + wave + i*kWaves, i < nb.  Their
+  // table entries are fetched 64 at a time, one per lane, and broadcast
+  // with readlane; the K/V slab of block i+1 is in flight while block i is
+  // being reduced.
+  const int nb = (blk_end - blk_begin - wave + kWaves - 1) / kWaves;
+  int tab = 0;
+  auto table_chunk = [&](int chunk) {
+    const int i = chunk * 64 + lane;
+    const int blk = blk_begin + wave + i * kWaves;
+    tab = (i < nb) ? bt[blk] : 0;
+  };
+  auto fetch = [&](int i, half8_t (&kr)[4], half8_t (&vr)[4]) {
+    if ((i & 63) == 0) table_chunk(i >> 6);
+    int phys = __builtin_amdgcn_readlane(tab, i & 63);
     if (phys < 0 || (int64_t)phys >= a.num_blocks) {
-      sm_bad = 1;
-      continue;
+      sm_bad = 1;  // the whole sequence reports NaN; read block 0 instead
+      phys = 0;
     }
-    const _Float16* kb = a.k_cache + (int64_t)phys * block_stride + head_off;
-    const _Float16* vb = a.v_cache + (int64_t)phys * block_stride + head_off;
-    half8_t kr[4], vr[4];
+    const _Float16* kb = a.k_cache + (int64_t)phys * block_stride + lane_off;
+    const _Float16* vb = a.v_cache + (int64_t)phys * block_stride + lane_off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(kb + (4 * i + grp) * D + 8 * dl));
-      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(vb + (4 * i + grp) * D + 8 * dl));
+    for (int u = 0; u < 4; ++u) {
+      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(kb + 4 * u * D));
+      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(vb + 4 * u * D));
     }
-    const int tok0 = blk * BS;
+  };
+  auto reduce = [&](int i, const half8_t (&kr)[4], const half8_t (&vr)[4]) {
+    const int tok0 = (blk_begin + wave + i * kWaves) * BS;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       float sc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float dot = row16_sum(dot8(qv[j], kr[i]));
-        sc[i] = (tok0 + 4 * i + grp < L) ? dot * a.scale_log2 : -INFINITY;
+      for (int u = 0; u < 4; ++u) {
+        const float dot = row16_sum(dot8(qv[j], kr[u]));
+        sc[u] = (tok0 + 4 * u + grp < L) ? dot * a.scale_log2 : -INFINITY;
       }
       const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       const float m_new = fmaxf(m[j], mx);
@@ -149,16 +174,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+      for (int u = 0; u < 4; ++u) p[u] = __builtin_amdgcn_exp2f(sc[u] - m_new);
       lsum[j] = lsum[j] * alpha + (p[0] + p[1]) + (p[2] + p[3]);
       m[j] = m_new;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         float acc = o[j][d] * alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc = fmaf(p[i], (float)vr[i][d], acc);
+        for (int u = 0; u < 4; ++u) acc = fmaf(p[u], (float)vr[u][d], acc);
         o[j][d] = acc;
       }
+    }
+  };
+
+  half8_t ka[4], va[4], kb2[4], vb2[4];
+  if (nb > 0) fetch(0, ka, va);
+  for (int i = 0; i < nb; i += 2) {
+    if (i + 1 < nb) fetch(i + 1, kb2, vb2);
+    reduce(i, ka, va);
+    if (i + 1 < nb) {
+      if (i + 2 < nb) fetch(i + 2, ka, va);
+      reduce(i + 1, kb2, vb2);
     }
   }
 
@@ -259,11 +295,15 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Largest split (in 16-token blocks) that still gives at least 8 workgroups
+// per CU over the table width: long splits amortise each workgroup's start-up
+// and partial write, many workgroups keep every CU's memory queue full.
 int decode_split_blocks(int num_seqs, int H_kv, int max_blocks_per_seq) {
-  (void)num_seqs;
-  (void)H_kv;
-  (void)max_blocks_per_seq;
-  return 32;  // 512 tokens per split
+  const int64_t pairs = (int64_t)num_seqs * H_kv;
+  const int64_t want = 8 * 256;
+  for (int split = 128; split > 16; split /= 2)
+    if (pairs * ((max_blocks_per_seq + split - 1) / split) >= want) return split;
+  return 16;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {

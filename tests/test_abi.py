@@ -98,14 +98,19 @@ def test_decode_rejects(lib, kw, want):
 
 
 def test_workspace_size(lib):
-    # 256 sequences, 16 q heads, tables of 256 blocks: 8 splits of 32 blocks,
-    # each split slot holds 128 fp32 outputs + (max, sum)
+    # 256 sequences x 8 kv heads, tables of 256 blocks: splits of 128 blocks
+    # (2 per sequence); each split slot holds 128 fp32 outputs + (max, sum)
     assert binding.attn_decode_paged_workspace_size(256, 16, 8, 128, 256, 16) == \
-        256 * 16 * 8 * (128 + 2) * 4
+        256 * 16 * 2 * (128 + 2) * 4
+    # 64 x 8 pairs, 2048-block tables: 16 splits of 128 blocks
     assert binding.attn_decode_paged_workspace_size(64, 16, 8, 128, 2048, 16) == \
-        64 * 16 * 64 * (128 + 2) * 4
-    # one split per sequence: no workspace
-    assert binding.attn_decode_paged_workspace_size(4, 16, 8, 128, 32, 16) == 0
+        64 * 16 * 16 * (128 + 2) * 4
+    # 4 x 8 pairs, 2048-block tables: the largest split that keeps
+    # pairs * splits >= 2048 is 32 blocks (64 splits)
+    assert binding.attn_decode_paged_workspace_size(4, 16, 8, 128, 2048, 16) == \
+        4 * 16 * 64 * (128 + 2) * 4
+    # a table that fits one split: no workspace
+    assert binding.attn_decode_paged_workspace_size(4, 16, 8, 128, 16, 16) == 0
     # invalid or unsupported shapes report 0
     assert binding.attn_decode_paged_workspace_size(4, 16, 8, 64, 256, 16) == 0
     assert binding.attn_decode_paged_workspace_size(0, 16, 8, 128, 256, 16) == 0
