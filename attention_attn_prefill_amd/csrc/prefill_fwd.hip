@@ -13,10 +13,10 @@
 //     H_q/H_kv is even, else 1) and 128 query rows of each: 4*HP wavefronts,
 //     each owning 32 rows of one head for the whole kernel.  Both heads read
 //     the same K/V tiles, so each tile is staged once for 2x the math;
-//   * keys stream through LDS in tiles of 64, double-buffered: K row-major
-//     [64][D+8] and V transposed [D][64+8] (the padding keeps the 16-byte MFMA
-//     operand reads free of bank conflicts).  The global loads of tile t+1 are
-//     issued before the math of tile t and land in LDS after it, so one
+//   * keys stream through LDS in tiles of 64, double-buffered, both row-major:
+//     K [64][D+8] and V [64][D+32] (the padding keeps the MFMA operand reads
+//     free of bank conflicts).  The global loads of the next tiles are issued
+//     before the math of the current one and land in LDS after it, so one
 //     barrier per tile suffices and the load latency hides behind the MFMAs;
 //   * per tile and wavefront:
 //       S^T[64 x 32] = K_tile[64 x D] . Q_w^T[D x 32]   (v_mfma_f32_32x32x16_f16)
@@ -24,10 +24,10 @@
 //     accumulator; the row max needs one v_permlane32_swap, the rest of the
 //     softmax is lane-local;
 //       O^T[D x 32] += V_tile^T[D x 64] . P^T[64 x 32]  (same instruction)
-//     where P^T is the score accumulator rounded to fp16 in place: the key
-//     order inside each 16-key chunk of the transposed V tile is permuted so
-//     that the accumulator layout of S^T is exactly the B-operand layout of
-//     P^T, with no data movement between lanes;
+//     where P^T is the score accumulator rounded to fp16 in place (no data
+//     movement between lanes), and the V^T operand is read from the
+//     row-major V tile with the transposing ds_read_b64_tr_b16, two reads per
+//     operand, in the key order that the S^T accumulator layout dictates;
 //   * online softmax with a lazy reference point: the running max used for
 //     the exponentials is only moved (and O, l rescaled) when a tile's max
 //     exceeds it by more than 2^8 in the exp2 domain.  The result is the same
@@ -65,12 +65,6 @@ __device__ __forceinline__ float wave_half_swap_add(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position group (of 4 keys) inside a 16-key chunk of the transposed V tile
-// for key group a = key/4 % 4: the B operand of the PV product for lane half
-// hf holds, at k = 8*hf + i, the score of key 4*hf + i (i < 4) or
-// 8 + 4*hf + (i - 4) (i >= 4), so key groups {0,1,2,3} sit at positions
-// {0,2,1,3}.
-__device__ __forceinline__ int vt_pos_group(int a) { return (a == 1) ? 2 : (a == 2) ? 1 : a; }
 
 // A raw buffer resource over [p, p + bytes).  The base address is passed
 // through readfirstlane so the descriptor lives in SGPRs (it is workgroup-
@@ -83,9 +77,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const _Float16* p, i
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// Row stride (halfs) of the V tile in LDS.  The PV operand is read with
+// ds_read_b64_tr_b16, where the 16 lanes of a group read 4 key rows x 16
+// dims; a stride of 16 dwords modulo the 64 banks keeps those rows on
+// disjoint banks.
+template <int D>
+struct VLayout {
+  static constexpr int VROW = (D == 32) ? 32 : D + 32;
+};
+
 // Per-thread staging of the K and V tiles: global -> registers (issued early)
-// -> LDS (written after the math of the current tile).  The K tile is written
-// row-major, the V tile transposed, 4 keys x 8 dims per work item.
+// -> LDS (written after the math of the current tile).  Both tiles are
+// written row-major, one 16-byte vector per (row, 8 dims).
 // Loads go through buffer resources whose range is the kv head's rows
 // [0, S_kv): rows past the end read as zeros (and are masked), with no
 // clamping arithmetic and 32-bit offsets.
@@ -93,15 +96,13 @@ template <int D, int HP>
 struct Stager {
   static constexpr int kThreads = 64 * kWavesPerHead * HP;
   static constexpr int VEC_PER_ROW = D / 8;                     // 16-byte vectors per key row
-  static constexpr int K_VECS = kBlockN * VEC_PER_ROW;
-  static constexpr int V_ITEMS = (kBlockN / 4) * VEC_PER_ROW;
-  static constexpr int K_PER_T = (K_VECS + kThreads - 1) / kThreads;
-  static constexpr int V_PER_T = (V_ITEMS + kThreads - 1) / kThreads;
+  static constexpr int VECS = kBlockN * VEC_PER_ROW;
+  static constexpr int PER_T = (VECS + kThreads - 1) / kThreads;
   static constexpr int KROW = D + 8;
-  static constexpr int VROW = kBlockN + 8;
+  static constexpr int VROW = VLayout<D>::VROW;
 
-  half8_t kreg[K_PER_T];
-  half8_t vreg[V_PER_T][4];
+  half8_t kreg[PER_T];
+  half8_t vreg[PER_T];
   __amdgpu_buffer_rsrc_t krsrc, vrsrc;
   int row_bytes;  // bytes between consecutive key rows (H_kv * D * 2)
 
@@ -112,55 +113,67 @@ struct Stager {
     krsrc = make_rsrc(kbase, range);
     vrsrc = make_rsrc(vbase, range);
   }
-  __device__ __forceinline__ static bool k_mine(int u, int tid) { return tid + u * kThreads < K_VECS; }
-  __device__ __forceinline__ static bool v_mine(int u, int tid) { return tid + u * kThreads < V_ITEMS; }
+  __device__ __forceinline__ static bool mine(int u, int tid) { return tid + u * kThreads < VECS; }
 
   __device__ __forceinline__ void load_k(int kv0, int tid) {
 #pragma unroll
-    for (int u = 0; u < K_PER_T; ++u) {
-      if (!k_mine(u, tid)) continue;
+    for (int u = 0; u < PER_T; ++u) {
+      if (!mine(u, tid)) continue;
       const int idx = tid + u * kThreads;
       const int r = idx / VEC_PER_ROW, c = idx % VEC_PER_ROW;
-      const int off = (kv0 + r) * row_bytes + 16 * c;
-      kreg[u] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off, 0, 0));
+      kreg[u] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(krsrc, (kv0 + r) * row_bytes + 16 * c, 0, 0));
     }
   }
   __device__ __forceinline__ void load_v(int kv0, int tid) {
 #pragma unroll
-    for (int u = 0; u < V_PER_T; ++u) {
-      if (!v_mine(u, tid)) continue;
+    for (int u = 0; u < PER_T; ++u) {
+      if (!mine(u, tid)) continue;
       const int idx = tid + u * kThreads;
-      const int kg = idx % (kBlockN / 4), c = idx / (kBlockN / 4);
-      const int off = (kv0 + 4 * kg) * row_bytes + 16 * c;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vreg[u][j] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off + j * row_bytes, 0, 0));
+      const int r = idx / VEC_PER_ROW, c = idx % VEC_PER_ROW;
+      vreg[u] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (kv0 + r) * row_bytes + 16 * c, 0, 0));
     }
   }
   __device__ __forceinline__ void store_k(_Float16* k_lds, int tid) const {
 #pragma unroll
-    for (int u = 0; u < K_PER_T; ++u) {
-      if (!k_mine(u, tid)) continue;
+    for (int u = 0; u < PER_T; ++u) {
+      if (!mine(u, tid)) continue;
       const int idx = tid + u * kThreads;
       const int r = idx / VEC_PER_ROW, c = idx % VEC_PER_ROW;
       *reinterpret_cast<half8_t*>(&k_lds[r * KROW + 8 * c]) = kreg[u];
     }
   }
-  __device__ __forceinline__ void store_v(_Float16* vt_lds, int tid) const {
+  __device__ __forceinline__ void store_v(_Float16* v_lds, int tid) const {
 #pragma unroll
-    for (int u = 0; u < V_PER_T; ++u) {
-      if (!v_mine(u, tid)) continue;
+    for (int u = 0; u < PER_T; ++u) {
+      if (!mine(u, tid)) continue;
       const int idx = tid + u * kThreads;
-      const int kg = idx % (kBlockN / 4), c = idx / (kBlockN / 4);
-      const int base = (8 * c) * VROW + (kg >> 2) * 16 + vt_pos_group(kg & 3) * 4;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        half4_t col4 = {vreg[u][0][i], vreg[u][1][i], vreg[u][2][i], vreg[u][3][i]};
-        *reinterpret_cast<half4_t*>(&vt_lds[base + i * VROW]) = col4;
-      }
+      const int r = idx / VEC_PER_ROW, c = idx % VEC_PER_ROW;
+      *reinterpret_cast<half8_t*>(&v_lds[r * VROW + 8 * c]) = vreg[u];
     }
   }
 };
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// 4 fp16 values through the transposing LDS read: in each 16-lane group,
+// lanes 4j..4j+3 read 16 consecutive halfs of row j and lane i receives
+// column i of rows 0..3.
+__device__ __forceinline__ short4_t lds_read_tr(const _Float16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(p));
+}
+
+// PV operand V^T[32 dims x 16 keys] for lane l: dims dt*32 + l%32, keys
+// 16c + 4*hf + (0..3) then 16c + 8 + 4*hf + (0..3) -- the key order of the
+// B operand taken straight from the S^T accumulator (registers 8(c%2)..+7 of
+// the 32-key half c/2).  `vl` already holds this lane's row/column offset.
+template <int VROW>
+__device__ __forceinline__ half8_t pv_operand(const _Float16* vl, int dt, int c) {
+  const short4_t lo = lds_read_tr(vl + 16 * c * VROW + dt * 32);
+  const short4_t hi = lds_read_tr(vl + (16 * c + 8) * VROW + dt * 32);
+  const short4_t lohi[2] = {lo, hi};
+  return __builtin_bit_cast(half8_t, lohi);
+}
 
 // S^T tile (64 keys x 32 queries) = K_tile . Q_w^T from an LDS K buffer.
 // The two 32-key accumulators alternate so consecutive MFMAs are
@@ -191,9 +204,9 @@ struct Prefill {
   static constexpr int KS = D / 16;         // k-steps of the QK^T contraction
   static constexpr int DT = D / 32;         // 32-wide d tiles of O^T
   static constexpr int KROW = D + 8;        // LDS row stride of K (halfs)
-  static constexpr int VROW = kBlockN + 8;  // LDS row stride of V^T (halfs)
+  static constexpr int VROW = VLayout<D>::VROW;  // LDS row stride of V (halfs)
   static constexpr int K_LDS = kBlockN * KROW;
-  static constexpr int V_LDS = D * VROW;
+  static constexpr int V_LDS = kBlockN * VROW;
 
   _Float16* k_lds;
   _Float16* vt_lds;
@@ -283,13 +296,12 @@ struct Prefill {
       constexpr int R = 4;
       half8_t ring[R];
 #pragma unroll
-      for (int n = 0; n < R; ++n) ring[n] = *reinterpret_cast<const half8_t*>(&vl[(n % DT) * 32 * VROW + 16 * (n / DT)]);
+      for (int n = 0; n < R; ++n) ring[n] = pv_operand<VROW>(vl, n % DT, n / DT);
 #pragma unroll
       for (int n = 0; n < N; ++n) {
         const int dt = n % DT, c = n / DT;
         const half8_t vf = ring[n % R];
-        if (n + R < N)
-          ring[n % R] = *reinterpret_cast<const half8_t*>(&vl[((n + R) % DT) * 32 * VROW + 16 * ((n + R) / DT)]);
+        if (n + R < N) ring[n % R] = pv_operand<VROW>(vl, (n + R) % DT, (n + R) / DT);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], o[dt], 0, 0, 0);
       }
     }
@@ -360,7 +372,9 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
   p.kbase = a.k + (int64_t)b * a.S_kv * p.kv_row_stride + (int64_t)g * D;
   p.vbase = a.v + (int64_t)b * a.S_kv * p.kv_row_stride + (int64_t)g * D;
   p.k_lane = col * P::KROW + 8 * p.hf;
-  p.v_lane = col * P::VROW + 8 * p.hf;
+  // transposed V reads: 16-lane group G = lane/16 covers dims 16*(G%2)..+15
+  // of keys 4*hf + (lane%16)/4, four dims per lane
+  p.v_lane = (4 * p.hf + (lane & 15) / 4) * P::VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // prologue: K(0), V(0) and K(1) into LDS
   p.st.init(p.kbase, p.vbase, (int)p.kv_row_stride, a.S_kv);
