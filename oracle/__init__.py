@@ -58,6 +58,8 @@ class Oracle:
         lib.oracle_half_to_double.restype = ctypes.c_double
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
+        lib.oracle_kv_append.argtypes = [P, P, P, P, P, I64, I, I, I, I64]
+        lib.oracle_kv_append.restype = I64
         self._lib = lib
         return lib
 
@@ -131,6 +133,28 @@ class Oracle:
         return (out, lse) if return_lse else out
 
 
+    def kv_append(self, k_new, v_new, k_cache, v_cache, slot_mapping):
+        """Copy new K/V rows [num_tokens, H_kv, D] into the paged caches
+        [num_blocks, H_kv, block_size, D] (modified in place) at
+        slot_mapping (int64, block*block_size + offset; -1 skipped).
+        Returns the number of tokens written."""
+        k_new, v_new = _f16(k_new), _f16(v_new)
+        if k_cache.dtype != np.float16 or v_cache.dtype != np.float16 or \
+                not k_cache.flags.c_contiguous or not v_cache.flags.c_contiguous:
+            raise TypeError("caches must be contiguous float16 arrays (updated in place)")
+        sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        num_tokens, H_kv, D = k_new.shape
+        num_blocks, H2, block_size, D2 = k_cache.shape
+        if v_new.shape != k_new.shape or v_cache.shape != k_cache.shape or H2 != H_kv or D2 != D \
+                or sm.shape != (num_tokens,):
+            raise ValueError("shape mismatch")
+        n = self._load().oracle_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(sm), num_tokens, H_kv, D, block_size, num_blocks)
+        if n < 0:
+            raise ValueError("oracle_kv_append rejected its arguments")
+        return int(n)
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -147,3 +171,4 @@ num_threads = default.num_threads
 half_to_double = default.half_to_double
 prefill = default.prefill
 decode_paged = default.decode_paged
+kv_append = default.kv_append

@@ -277,3 +277,43 @@ int oracle_decode_paged(const uint16_t* q, const uint16_t* k_cache,
   }
   return err ? -1 : 0;
 }
+
+/* ---- paged KV append ---------------------------------------------------- */
+/* The write side of the paged cache ("GRPO-CUDA Project Memory", "KV Cache
+ * design" section: slot_mapping[token] = physical_block * block_size +
+ * in-block offset, int64; "Known bugs fixed": padding tokens carry slot -1
+ * and are skipped).  Token i's rows k_new[i, h, :] and v_new[i, h, :] (new
+ * keys/values laid out [num_tokens, H_kv, D]) are copied to
+ * cache[slot / block_size, h, slot % block_size, :] for every head h.
+ * Readings: any slot outside [0, num_blocks * block_size) is skipped like -1;
+ * tokens are applied in order, so a repeated slot keeps the last token's rows
+ * (the GPU leaves repeated slots unspecified and no test uses them).
+ * Returns the number of tokens written, or -1 on invalid arguments.          */
+int64_t oracle_kv_append(const uint16_t* k_new, const uint16_t* v_new,
+                         uint16_t* k_cache, uint16_t* v_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens,
+                         int H_kv, int D, int block_size, int64_t num_blocks) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return -1;
+  if (num_tokens < 0 || H_kv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0)
+    return -1;
+  const int64_t capacity = num_blocks * (int64_t)block_size;
+  int64_t written = 0;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= capacity) continue;
+    const int64_t block = slot / block_size;
+    const int64_t off = slot % block_size;
+    for (int h = 0; h < H_kv; ++h) {
+      const uint16_t* ks = k_new + (i * H_kv + h) * (int64_t)D;
+      const uint16_t* vs = v_new + (i * H_kv + h) * (int64_t)D;
+      uint16_t* kd = k_cache + ((block * H_kv + h) * block_size + off) * (int64_t)D;
+      uint16_t* vd = v_cache + ((block * H_kv + h) * block_size + off) * (int64_t)D;
+      for (int d = 0; d < D; ++d) {
+        kd[d] = ks[d];
+        vd[d] = vs[d];
+      }
+    }
+    ++written;
+  }
+  return written;
+}

@@ -325,4 +325,73 @@ def pin_rejects_invalid(ora):
         raise AssertionError("invalid arguments were accepted")
 
 
+
+
+# ---- paged KV append (write side of the cache) ---------------------------------
+
+def _slots_for(lens, bt, block_size=16):
+    """slot of every token of every sequence, in (sequence, token) order."""
+    out = []
+    for s, L in enumerate(lens):
+        for t in range(L):
+            out.append(int(bt[s, t // block_size]) * block_size + t % block_size)
+    return np.array(out, np.int64)
+
+
+def pin_kv_append_placement(ora):
+    """Each token's rows land at [slot // 16, h, slot % 16, :]; checked against
+    numpy fancy indexing on a token-major view of the cache."""
+    H, D, bs, nb = 3, 16, 16, 5
+    rng = np.random.default_rng(101)
+    kc = _rand16((nb, H, bs, D), 102)
+    vc = _rand16((nb, H, bs, D), 103)
+    n = 23
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    kn, vn = _rand16((n, H, D), 104), _rand16((n, H, D), 105)
+    want_k = kc.transpose(0, 2, 1, 3).reshape(nb * bs, H, D).copy()
+    want_v = vc.transpose(0, 2, 1, 3).reshape(nb * bs, H, D).copy()
+    want_k[slots] = kn
+    want_v[slots] = vn
+    got = ora.kv_append(kn, vn, kc, vc, slots)
+    assert got == n
+    assert np.array_equal(kc.transpose(0, 2, 1, 3).reshape(nb * bs, H, D), want_k)
+    assert np.array_equal(vc.transpose(0, 2, 1, 3).reshape(nb * bs, H, D), want_v)
+
+
+def pin_kv_append_skips_padding(ora):
+    """Slot -1 (padding) and slots past the pool leave the cache untouched."""
+    H, D, bs, nb = 2, 8, 16, 3
+    kc, vc = _rand16((nb, H, bs, D), 106), _rand16((nb, H, bs, D), 107)
+    k0, v0 = kc.copy(), vc.copy()
+    kn, vn = _rand16((4, H, D), 108), _rand16((4, H, D), 109)
+    slots = np.array([-1, nb * bs, -1, nb * bs + 5], np.int64)
+    assert ora.kv_append(kn, vn, kc, vc, slots) == 0
+    assert np.array_equal(kc, k0) and np.array_equal(vc, v0)
+    slots[1] = 0  # one valid slot among the padding
+    assert ora.kv_append(kn, vn, kc, vc, slots) == 1
+    assert np.array_equal(kc[0, :, 0], kn[1]) and np.array_equal(vc[0, :, 0], vn[1])
+    kc[0, :, 0], vc[0, :, 0] = k0[0, :, 0], v0[0, :, 0]
+    assert np.array_equal(kc, k0) and np.array_equal(vc, v0)
+
+
+def pin_append_then_decode_equals_prefill(ora):
+    """Appending a sequence's K/V through a permuted table and decoding its
+    last query reproduces the last row of causal prefill."""
+    H_q, H_kv, D, bs = 4, 2, 32, 16
+    lens = [37, 16, 5]
+    T = max(lens)
+    Q, K, V = _rand16((3, T, H_q, D), 110), _rand16((3, T, H_kv, D), 111), _rand16((3, T, H_kv, D), 112)
+    bt, nb = W.paged_layout(lens, bs, 4, (9, 9))
+    kc = np.zeros((nb, H_kv, bs, D), np.float16)
+    vc = np.zeros_like(kc)
+    kn = np.concatenate([K[s, :L] for s, L in enumerate(lens)])
+    vn = np.concatenate([V[s, :L] for s, L in enumerate(lens)])
+    assert ora.kv_append(kn, vn, kc, vc, _slots_for(lens, bt)) == sum(lens)
+    q_last = np.stack([Q[s, L - 1] for s, L in enumerate(lens)])
+    od = ora.decode_paged(q_last, kc, vc, bt, np.array(lens, np.int32))
+    for s, L in enumerate(lens):
+        op = ora.prefill(Q[s:s + 1, :L], K[s:s + 1, :L], V[s:s + 1, :L], causal=True)
+        assert np.allclose(od[s], op[0, L - 1], rtol=0, atol=1e-14), (s, L)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -28,6 +28,12 @@ MUTANTS = [
     ("binary16 subnormal scale", "ldexp((double)f, -24)", "ldexp((double)f, -23)"),
     ("LSE without the max", "*lse = m + log(z);", "*lse = log(z);"),
     ("score of key 0 skipped in max", "double m = scores[0];", "double m = scores[n - 1];\n  if (n > 1) m = scores[1];"),
+    ("append: in-block offset shifted", "const int64_t off = slot % block_size;",
+     "const int64_t off = (slot + 1) % block_size;"),
+    ("append: slot 0 treated as padding", "if (slot < 0 || slot >= capacity) continue;",
+     "if (slot <= 0 || slot >= capacity) continue;"),
+    ("append: heads swapped", "uint16_t* kd = k_cache + ((block * H_kv + h) * block_size + off) * (int64_t)D;",
+     "uint16_t* kd = k_cache + ((block * H_kv + (H_kv - 1 - h)) * block_size + off) * (int64_t)D;"),
 ]
 
 
