@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     attn_abi_version,
     attn_decode_paged,
     attn_decode_paged_workspace_size,
+    attn_kv_append,
     attn_prefill,
     attn_status_string,
     load_library,

@@ -48,6 +48,8 @@ def load_library():
     lib.attn_decode_paged_workspace_size.restype = SZ
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I64, P, SZ, P]
     lib.attn_decode_paged.restype = I
+    lib.attn_kv_append.argtypes = [P, P, P, P, P, I64, I, I, I, I64, P]
+    lib.attn_kv_append.restype = I
     _lib = lib
     return lib
 
@@ -135,3 +137,27 @@ def attn_decode_paged(q, k_cache, v_cache, out, block_tables, seq_lens, workspac
                                           ws, ws_bytes, _stream_handle(stream, q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_paged")
+
+
+def attn_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """Write new K/V rows into the paged caches via ``attn_kv_append``.
+
+    k_new/v_new [num_tokens, H_kv, D] float16 (a [B, S, H_kv, D] prefill
+    tensor is accepted and read as B*S tokens); caches
+    [num_blocks, H_kv, block_size, D] float16, updated in place;
+    slot_mapping [num_tokens] int64 (-1 = padding, skipped).
+    """
+    import torch
+    H_kv, D = k_new.shape[-2], k_new.shape[-1]
+    num_tokens = k_new.numel() // (H_kv * D)
+    num_blocks, H2, block_size, D2 = k_cache.shape
+    if tuple(v_new.shape) != tuple(k_new.shape) or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or H2 != H_kv or D2 != D or slot_mapping.numel() != num_tokens:
+        raise ValueError("shape mismatch between new rows, caches and slot_mapping")
+    ptrs = [_dev_tensor(x, torch.float16, n) for x, n in
+            ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"))]
+    sm = _dev_tensor(slot_mapping, torch.int64, "slot_mapping")
+    st = load_library().attn_kv_append(*ptrs, sm, num_tokens, H_kv, D, block_size, num_blocks,
+                                       _stream_handle(stream, k_new.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_kv_append")

@@ -154,3 +154,31 @@ ATTN_EXPORT attn_status_t attn_decode_paged(const void* q, const void* k_cache, 
   const hipError_t e = attn::launch_decode(a, H_q / H_kv, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
+
+ATTN_EXPORT attn_status_t attn_kv_append(const void* k_new, const void* v_new, void* k_cache,
+                                         void* v_cache, const int64_t* slot_mapping,
+                                         int64_t num_tokens, int H_kv, int head_dim, int block_size,
+                                         int64_t num_blocks, void* stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return ATTN_ERR_INVALID_ARG;
+  if (num_tokens < 0 || H_kv <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (head_dim % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return ATTN_ERR_INVALID_ARG;
+  if (ceil_div64(num_tokens, 4) > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return ATTN_OK;
+  attn::KvAppendArgs a;
+  a.k_new = static_cast<const _Float16*>(k_new);
+  a.v_new = static_cast<const _Float16*>(v_new);
+  a.k_cache = static_cast<_Float16*>(k_cache);
+  a.v_cache = static_cast<_Float16*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_blocks = num_blocks;
+  a.H_kv = H_kv;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  const hipError_t e = attn::launch_kv_append(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

@@ -42,9 +42,21 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+struct KvAppendArgs {
+  const _Float16* k_new;  // [num_tokens, H_kv, head_dim]
+  const _Float16* v_new;
+  _Float16* k_cache;      // [num_blocks, H_kv, block_size, head_dim]
+  _Float16* v_cache;
+  const int64_t* slot_mapping;  // [num_tokens]
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int H_kv, head_dim, block_size;
+};
+
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 
 // Decode split policy (shared by the workspace-size query and the launch).
 constexpr int kDecodeBlockSize = 16;

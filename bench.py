@@ -124,6 +124,38 @@ def cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl, target_s):
     }
 
 
+def time_kv_append(pcfg, k, v, dev, stream, W, iters=100):
+    """The prefill's K/V (B*S tokens) written into a paged cache through a
+    permuted block table: HBM bytes = read + write of every row."""
+    import torch
+
+    from attention_attn_prefill_amd import attn_kv_append
+    lens = [pcfg.S_kv] * pcfg.B
+    bt, nb = W.paged_layout(lens, 16, (pcfg.S_kv + 15) // 16, (11, 11))
+    slots = np.concatenate([bt[s, np.arange(L) // 16].astype(np.int64) * 16 + np.arange(L) % 16
+                            for s, L in enumerate(lens)])
+    kn = torch.from_numpy(k).to(dev).view(-1, pcfg.H_kv, pcfg.D)
+    vn = torch.from_numpy(v).to(dev).view(-1, pcfg.H_kv, pcfg.D)
+    kc = torch.empty((nb, pcfg.H_kv, 16, pcfg.D), dtype=torch.float16, device=dev)
+    vc = torch.empty_like(kc)
+    sm = torch.from_numpy(slots).to(dev)
+    for _ in range(20):
+        attn_kv_append(kn, vn, kc, vc, sm, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        attn_kv_append(kn, vn, kc, vc, sm, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = 2 * 2 * kn.numel() * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "paged KV append GB/s (read + write)", "value": round(gbs, 1), "unit": "GB/s",
+            "tokens": int(kn.shape[0]), "bytes": int(nbytes), "launch_ms": round(ms, 5),
+            "roofline": {"bound": "hbm", "kernel": "kv_append_kernel", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -243,6 +275,7 @@ def main():
             },
         },
     }
+    line["kv_append"] = time_kv_append(pcfg, k, v, dev, stream, W)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl,

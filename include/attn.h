@@ -126,6 +126,30 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * Paged KV append: write new keys and values into the paged caches that
+ * attn_decode_paged reads -- the write side of the same data structure
+ * ("GRPO-CUDA Project Memory" page, "KV Cache design": slot_mapping[token] =
+ * physical_block * block_size + in-block offset, int64; "Known bugs fixed":
+ * padding tokens carry slot -1 and are skipped).
+ *
+ *   k_new, v_new  [num_tokens, H_kv, head_dim] fp16 (e.g. a prefill's K/V
+ *                 [B, S, H_kv, D] seen as B*S tokens)
+ *   k_cache, v_cache [num_blocks, H_kv, block_size, head_dim] fp16 (updated)
+ *   slot_mapping  [num_tokens] int64
+ *
+ * Token i's rows go to cache[slot / block_size, h, slot % block_size, :] for
+ * every head h.  Slots outside [0, num_blocks * block_size), -1 included,
+ * are skipped.  Two tokens with the same slot race (the result for that slot
+ * is unspecified).  head_dim must be a multiple of 8; any block_size >= 1.
+ * num_tokens == 0 is a no-op.
+ */
+attn_status_t attn_kv_append(const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, int64_t num_tokens,
+                             int H_kv, int head_dim, int block_size,
+                             int64_t num_blocks, void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "attn_abi_version", "attn_status_string", "attn_prefill",
-        "attn_decode_paged_workspace_size", "attn_decode_paged"])
+        "attn_decode_paged_workspace_size", "attn_decode_paged", "attn_kv_append"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -121,3 +121,18 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         binding.load_library()
+
+
+def append(lib, kn=P, vn=P, kc=P2, vc=P2, sm=P, n=16, H_kv=8, D=128, bs=16, nb=4):
+    return lib.attn_kv_append(kn, vn, kc, vc, sm, n, H_kv, D, bs, nb, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kn=NULL), INV), (dict(vn=NULL), INV), (dict(kc=NULL), INV), (dict(vc=NULL), INV),
+    (dict(sm=NULL), INV), (dict(n=-1), INV), (dict(H_kv=0), INV), (dict(D=0), INV),
+    (dict(bs=0), INV), (dict(nb=0), INV), (dict(D=36), UNS),
+    (dict(kc=ctypes.c_void_p(0x20008)), INV), (dict(sm=ctypes.c_void_p(0x10004)), INV),
+    (dict(n=0), OK),   # nothing to do: returns without touching the GPU
+])
+def test_kv_append_rejects(lib, kw, want):
+    assert append(lib, **kw) == want
