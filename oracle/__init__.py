@@ -11,7 +11,9 @@ in fp64 over the exact values of binary16 inputs.  Prefill follows the
 attention.cuh / test_attention.cu listings of "Tutorial: Adding a New Kernel to
 RL.cu" (layout [B,S,H,D], GQA kv head = h*H_kv//H_q, causal row i sees keys
 0..i); paged decode follows the decode section of the same listing and the
-"KV Cache design" section of the GRPO-CUDA project memory page.
+"KV Cache design" section of the GRPO-CUDA project memory page; QK-norm and
+the NeoX rotary embedding follow the "Qwen3" and "RoPE design" sections of the
+same page.
 
 Every function here is pinned by tests in ``tests/test_oracle_pins.py``
 (closed forms, invariants, a library routine on special cases, brute force on
@@ -60,6 +62,11 @@ class Oracle:
         lib.oracle_num_threads.restype = I
         lib.oracle_kv_append.argtypes = [P, P, P, P, P, I64, I, I, I, I64]
         lib.oracle_kv_append.restype = I64
+        D_ = ctypes.c_double
+        lib.oracle_rope_table.argtypes = [P, P, I, I, D_]
+        lib.oracle_rope_table.restype = I
+        lib.oracle_qk_norm_rope.argtypes = [P, P, P, P, P, I64, I, I, I, D_, P]
+        lib.oracle_qk_norm_rope.restype = I
         self._lib = lib
         return lib
 
@@ -154,6 +161,39 @@ class Oracle:
             raise ValueError("oracle_kv_append rejected its arguments")
         return int(n)
 
+    def rope_table(self, max_pos: int, D: int, theta: float):
+        """fp64 (cos, sin) tables [max_pos, D/2] of the NeoX rotation:
+        angle pos * theta^(-2i/D)."""
+        cos = np.empty((max_pos, D // 2), np.float64)
+        sin = np.empty((max_pos, D // 2), np.float64)
+        rc = self._load().oracle_rope_table(_ptr(cos), _ptr(sin), int(max_pos), int(D), float(theta))
+        if rc != 0:
+            raise ValueError("oracle_rope_table rejected its arguments")
+        return cos, sin
+
+    def qk_norm_rope(self, x, weight, positions, cos, sin, eps: float = 1e-6):
+        """Per-head RMSNorm (skipped when ``weight`` is None) then NeoX
+        split-half rotation of x [n_tokens, H, D] (float16) at int32
+        ``positions``, with fp64 tables [max_pos, D/2].  Returns float64
+        [n_tokens, H, D]; rows of out-of-range positions are NaN."""
+        x = _f16(x)
+        n_tokens, H, D = x.shape
+        w = None if weight is None else _f16(weight)
+        if w is not None and w.shape != (D,):
+            raise ValueError("weight must be [D]")
+        pos = np.ascontiguousarray(positions, dtype=np.int32)
+        cos = np.ascontiguousarray(cos, dtype=np.float64)
+        sin = np.ascontiguousarray(sin, dtype=np.float64)
+        if pos.shape != (n_tokens,) or cos.shape != sin.shape or cos.ndim != 2 or \
+                cos.shape[1] != D // 2:
+            raise ValueError("shape mismatch")
+        out = np.empty((n_tokens, H, D), np.float64)
+        rc = self._load().oracle_qk_norm_rope(_ptr(x), _ptr(w), _ptr(pos), _ptr(cos), _ptr(sin),
+                                              n_tokens, H, D, cos.shape[0], float(eps), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_qk_norm_rope rejected its arguments")
+        return out
+
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
@@ -172,3 +212,5 @@ half_to_double = default.half_to_double
 prefill = default.prefill
 decode_paged = default.decode_paged
 kv_append = default.kv_append
+rope_table = default.rope_table
+qk_norm_rope = default.qk_norm_rope

@@ -317,3 +317,78 @@ int64_t oracle_kv_append(const uint16_t* k_new, const uint16_t* v_new,
   }
   return written;
 }
+
+/* ---- RoPE table ------------------------------------------------------------ */
+/* "GRPO-CUDA Project Memory", "RoPE design": a table of [max_seq_len, D/2]
+ * entries precomputed once and read by the rotation.  Pair i of a head
+ * turns by the angle pos * inv_freq[i], inv_freq[i] = theta^(-2i/D) (the
+ * frequency the cross-attention trace spells 1/(base^(arange(0,D,2)/D))).
+ * The pages do not give theta: it is a parameter (Qwen3 configurations use
+ * 1e6; 1e4 is the classic value).  Here the angle, cosine and sine are fp64.
+ * Returns 0, or -1 on invalid arguments.                                     */
+int oracle_rope_table(double* cos_out, double* sin_out, int max_pos, int D, double theta) {
+  if (!cos_out || !sin_out || max_pos <= 0 || D <= 0 || (D & 1) || !(theta > 0.0)) return -1;
+  const int half = D / 2;
+  for (int p = 0; p < max_pos; ++p) {
+    for (int i = 0; i < half; ++i) {
+      const double inv_freq = pow(theta, -2.0 * (double)i / (double)D);
+      const double angle = (double)p * inv_freq;
+      cos_out[(int64_t)p * half + i] = cos(angle);
+      sin_out[(int64_t)p * half + i] = sin(angle);
+    }
+  }
+  return 0;
+}
+
+/* ---- QK-norm + NeoX RoPE ------------------------------------------------- */
+/* Qwen3 order ("GRPO-CUDA Project Memory", "Qwen3 key dims" and "Qwen3-
+ * Specific Notes"): RMSNorm over each head's D values first, then the
+ * rotary embedding.
+ *   RMSNorm (per token and head, eps given; the pages' models use 1e-6):
+ *     y_d = x_d / sqrt((1/D) * sum_e x_e^2 + eps) * w_d
+ *   NeoX split-half rotation ("RoPE design"), for i in [0, D/2):
+ *     out_i       = y_i * cos_i - y_{i+D/2} * sin_i
+ *     out_{i+D/2} = y_{i+D/2} * cos_i + y_i * sin_i
+ *   with cos_i, sin_i the table entries of the token's position.
+ * x: [n_tokens, H, D] binary16; weight: [D] binary16, or NULL for rotation
+ * only; positions: int32 [n_tokens]; tables: fp64 [max_pos, D/2].
+ * Reading: a position outside [0, max_pos) has no table row; the token's
+ * rows come out NaN (the GPU path does the same).  The norm and the rotation
+ * are evaluated without intermediate rounding (the fused GPU kernel keeps
+ * fp32 between them).
+ * Returns 0, or -1 on invalid arguments.                                     */
+int oracle_qk_norm_rope(const uint16_t* x, const uint16_t* weight, const int32_t* positions,
+                        const double* cos_t, const double* sin_t, int64_t n_tokens, int H,
+                        int D, int max_pos, double eps, double* out) {
+  if (!x || !positions || !cos_t || !sin_t || !out) return -1;
+  if (n_tokens < 0 || H <= 0 || D <= 0 || (D & 1) || max_pos <= 0 || eps < 0.0) return -1;
+  const int half = D / 2;
+  double* y = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!y) return -1;
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    const int32_t pos = positions[t];
+    for (int h = 0; h < H; ++h) {
+      const uint16_t* xr = x + (t * H + h) * (int64_t)D;
+      double* o = out + (t * H + h) * (int64_t)D;
+      if (pos < 0 || pos >= max_pos) {
+        for (int d = 0; d < D; ++d) o[d] = NAN;
+        continue;
+      }
+      for (int d = 0; d < D; ++d) y[d] = half_bits_to_double(xr[d]);
+      if (weight) {
+        double ss = 0.0;
+        for (int d = 0; d < D; ++d) ss += y[d] * y[d];
+        const double r = sqrt(ss / (double)D + eps);
+        for (int d = 0; d < D; ++d) y[d] = y[d] / r * half_bits_to_double(weight[d]);
+      }
+      const double* c = cos_t + (int64_t)pos * half;
+      const double* s = sin_t + (int64_t)pos * half;
+      for (int i = 0; i < half; ++i) {
+        o[i] = y[i] * c[i] - y[i + half] * s[i];
+        o[i + half] = y[i + half] * c[i] + y[i] * s[i];
+      }
+    }
+  }
+  free(y);
+  return 0;
+}

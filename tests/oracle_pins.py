@@ -23,6 +23,16 @@ What pins what:
   * paging                   -- decode equals the last causal-prefill row,
                                 block-permutation invariance, a brute-force
                                 scipy softmax over the gathered context
+  * KV append                -- numpy fancy indexing; padding slots; append
+                                then decode equals prefill
+  * RoPE table               -- the pages' printed frequency formula (numpy
+                                arange) recovered with atan2; cos^2+sin^2 = 1;
+                                angle addition across positions
+  * NeoX rotation            -- numpy complex multiplication; position 0 is
+                                the identity; norms kept; only m - n matters
+  * QK RMSNorm               -- unit mean square, scale invariance, a
+                                constant-row closed form (mean, eps, weight);
+                                numpy RMSNorm then rotation (the pages' order)
 """
 from __future__ import annotations
 
@@ -392,6 +402,133 @@ def pin_append_then_decode_equals_prefill(ora):
     for s, L in enumerate(lens):
         op = ora.prefill(Q[s:s + 1, :L], K[s:s + 1, :L], V[s:s + 1, :L], causal=True)
         assert np.allclose(od[s], op[0, L - 1], rtol=0, atol=1e-14), (s, L)
+
+
+# ---- QK-norm + NeoX RoPE ------------------------------------------------------
+
+def _np_inv_freq(D, base):
+    # the frequency as the cross-attention trace prints it: 1/(base^(arange(0,D,2)/D))
+    return 1.0 / (base ** (np.arange(0, D, 2, dtype=np.float64) / D))
+
+
+def _np_rotate(y, pos, base):
+    """NeoX split-half rotation as a complex product: (y_i + i*y_{i+D/2}) *
+    exp(i*pos*inv_freq_i), written with numpy's complex arithmetic."""
+    D = y.shape[-1]
+    z = y[..., : D // 2] + 1j * y[..., D // 2:]
+    ang = np.asarray(pos, np.float64)[:, None, None] * _np_inv_freq(D, base)[None, None, :]
+    r = z * np.exp(1j * ang)
+    return np.concatenate([r.real, r.imag], axis=-1)
+
+
+def pin_rope_table_frequency_and_angle_addition(ora):
+    """Position 1 holds the pages' frequencies (recovered with atan2, every
+    angle is below pi there); cos^2 + sin^2 = 1; and row p+q is row p turned
+    by row q (the angle is linear in the position)."""
+    for D, base in ((128, 1e4), (128, 1e6), (64, 5e5), (32, 1e4)):
+        c, s = ora.rope_table(64, D, base)
+        assert np.allclose(np.arctan2(s[1], c[1]), _np_inv_freq(D, base), rtol=1e-14, atol=0)
+        assert np.allclose(c * c + s * s, 1.0, rtol=0, atol=1e-15)
+        assert np.array_equal(c[0], np.ones(D // 2)) and np.array_equal(s[0], np.zeros(D // 2))
+        for p_, q_ in ((3, 5), (17, 29), (1, 62)):
+            zc = (c[p_] + 1j * s[p_]) * (c[q_] + 1j * s[q_])
+            assert np.allclose(zc.real, c[p_ + q_], atol=1e-13) and np.allclose(zc.imag, s[p_ + q_], atol=1e-13)
+
+
+def pin_rope_position_zero_is_identity(ora):
+    x = _rand16((5, 3, 64), 201)
+    c, s = ora.rope_table(4, 64, 1e4)
+    out = ora.qk_norm_rope(x, None, np.zeros(5, np.int32), c, s)
+    assert np.array_equal(out, _f64(x))
+
+
+def pin_rope_matches_complex_rotation(ora):
+    """Rotation only (no weight): the oracle equals the complex product at
+    random positions, for D in {32, 64, 128} and two bases."""
+    for D, base in ((128, 1e6), (64, 1e4), (32, 1e4)):
+        x = _rand16((9, 4, D), 202 + D)
+        pos = np.random.default_rng(203).integers(0, 4096, 9).astype(np.int32)
+        c, s = ora.rope_table(4096, D, base)
+        got = ora.qk_norm_rope(x, None, pos, c, s)
+        assert np.allclose(got, _np_rotate(_f64(x), pos, base), rtol=0, atol=1e-12)
+
+
+def pin_rope_preserves_norm_and_depends_on_offset_only(ora):
+    """A rotation keeps every head's norm; <R(m) q, R(n) k> depends on m - n."""
+    D = 128
+    c, s = ora.rope_table(3000, D, 1e6)
+    q, k = _rand16((1, 2, D), 204), _rand16((1, 2, D), 205)
+    qr = lambda p: ora.qk_norm_rope(q, None, np.array([p], np.int32), c, s)
+    kr = lambda p: ora.qk_norm_rope(k, None, np.array([p], np.int32), c, s)
+    assert np.allclose(np.linalg.norm(qr(1234), axis=-1), np.linalg.norm(_f64(q), axis=-1), rtol=1e-14)
+    for m, n, dlt in ((10, 3, 500), (700, 2900, -650), (0, 0, 2999)):
+        a = np.sum(qr(m) * kr(n), axis=-1)
+        b = np.sum(qr(m + dlt) * kr(n + dlt), axis=-1)
+        assert np.allclose(a, b, rtol=1e-11, atol=1e-11), (m, n, dlt)
+
+
+def pin_rmsnorm_unit_mean_square_and_scale_invariance(ora):
+    """With unit weight and eps 0 the rows have mean square 1, and scaling
+    the input by 2 (exact in binary16) changes nothing."""
+    D = 128
+    c, s = ora.rope_table(2, D, 1e4)
+    x = _rand16((6, 5, D), 206)
+    w = np.ones(D, np.float16)
+    y = ora.qk_norm_rope(x, w, np.zeros(6, np.int32), c, s, eps=0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-14)
+    y2 = ora.qk_norm_rope((x.astype(np.float32) * 2).astype(np.float16), w, np.zeros(6, np.int32), c, s, eps=0.0)
+    assert np.allclose(y, y2, rtol=1e-15, atol=0)
+
+
+def pin_rmsnorm_constant_row_closed_form(ora):
+    """A row of D equal values a gives a / sqrt(a^2 + eps) * w_d (position 0),
+    which pins the mean (not the sum), eps inside the root and the weight."""
+    D = 64
+    c, s = ora.rope_table(1, D, 1e4)
+    w = _rand16((D,), 207)
+    for a, eps in ((0.5, 1e-6), (0.01, 1e-3), (3.0, 0.25)):
+        x = np.full((1, 1, D), a, np.float16)
+        av = float(x[0, 0, 0])
+        got = ora.qk_norm_rope(x, w, np.zeros(1, np.int32), c, s, eps=eps)[0, 0]
+        assert np.allclose(got, av / math.sqrt(av * av + eps) * _f64(w), rtol=1e-14, atol=0), (a, eps)
+    zero = ora.qk_norm_rope(np.zeros((1, 1, D), np.float16), w, np.zeros(1, np.int32), c, s, eps=1e-6)
+    assert np.array_equal(zero, np.zeros((1, 1, D)))
+
+
+def pin_norm_then_rope_against_numpy(ora):
+    """Non-uniform weight at random positions: the oracle equals numpy's
+    RMSNorm followed by the complex rotation, and differs from the opposite
+    order (the pages put QK-norm before RoPE)."""
+    D, eps, base = 128, 1e-6, 1e6
+    x = _rand16((7, 3, D), 208, scale=2.0)
+    w = (np.random.default_rng(209).uniform(0.2, 2.0, D)).astype(np.float16)
+    pos = np.random.default_rng(210).integers(1, 2048, 7).astype(np.int32)
+    c, s = ora.rope_table(2048, D, base)
+    got = ora.qk_norm_rope(x, w, pos, c, s, eps=eps)
+    xf = _f64(x)
+    y = xf / np.sqrt(np.mean(xf * xf, axis=-1, keepdims=True) + eps) * _f64(w)
+    assert np.allclose(got, _np_rotate(y, pos, base), rtol=0, atol=1e-12)
+    r = _np_rotate(xf, pos, base)
+    other = r / np.sqrt(np.mean(r * r, axis=-1, keepdims=True) + eps) * _f64(w)
+    assert not np.allclose(got, other, atol=1e-3)
+
+
+def pin_rope_bad_position_gives_nan_row(ora):
+    D = 32
+    c, s = ora.rope_table(8, D, 1e4)
+    x = _rand16((4, 2, D), 211)
+    out = ora.qk_norm_rope(x, None, np.array([3, -1, 8, 7], np.int32), c, s)
+    assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
+    assert not np.isnan(out[0]).any() and not np.isnan(out[3]).any()
+
+
+def pin_rope_rejects_invalid(ora):
+    for args in ((4, 7, 1e4), (0, 8, 1e4), (4, 8, 0.0)):
+        try:
+            ora.rope_table(*args)
+        except ValueError:
+            continue
+        raise AssertionError(f"rope_table accepted {args}")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

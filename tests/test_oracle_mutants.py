@@ -34,6 +34,23 @@ MUTANTS = [
      "if (slot <= 0 || slot >= capacity) continue;"),
     ("append: heads swapped", "uint16_t* kd = k_cache + ((block * H_kv + h) * block_size + off) * (int64_t)D;",
      "uint16_t* kd = k_cache + ((block * H_kv + (H_kv - 1 - h)) * block_size + off) * (int64_t)D;"),
+    ("rope table: frequency exponent -i/D", "pow(theta, -2.0 * (double)i / (double)D)",
+     "pow(theta, -1.0 * (double)i / (double)D)"),
+    ("rope table: cos and sin swapped", "cos_out[(int64_t)p * half + i] = cos(angle);",
+     "cos_out[(int64_t)p * half + i] = sin(angle);"),
+    ("rope: first-half sign flipped", "o[i] = y[i] * c[i] - y[i + half] * s[i];",
+     "o[i] = y[i] * c[i] + y[i + half] * s[i];"),
+    ("rope: second-half sign flipped", "o[i + half] = y[i + half] * c[i] + y[i] * s[i];",
+     "o[i + half] = y[i + half] * c[i] - y[i] * s[i];"),
+    ("rope: adjacent pairs instead of split halves", "o[i] = y[i] * c[i] - y[i + half] * s[i];",
+     "o[i] = y[i] * c[i] - y[i ^ 1] * s[i];"),
+    ("rope: previous position's table row", "const double* c = cos_t + (int64_t)pos * half;",
+     "const double* c = cos_t + (int64_t)(pos > 0 ? pos - 1 : 0) * half;"),
+    ("rmsnorm: eps outside the root", "sqrt(ss / (double)D + eps)", "(sqrt(ss / (double)D) + eps)"),
+    ("rmsnorm: sum instead of mean", "sqrt(ss / (double)D + eps)", "sqrt(ss + eps)"),
+    ("rmsnorm: weight dropped", "y[d] = y[d] / r * half_bits_to_double(weight[d]);", "y[d] = y[d] / r;"),
+    ("rmsnorm: weight reversed", "y[d] = y[d] / r * half_bits_to_double(weight[d]);",
+     "y[d] = y[d] / r * half_bits_to_double(weight[D - 1 - d]);"),
 ]
 
 
