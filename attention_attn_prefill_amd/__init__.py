@@ -1,5 +1,6 @@
 """MI355X (gfx950) scaled-dot-product attention: causal GQA prefill and
-paged single-token decode behind the C ABI of libattn.so (include/attn.h).
+paged single-token decode behind the C ABI of libattn.so (include/attn.h),
+with the paged KV append and the fused QK-norm + rotary step around them.
 
 ``binding`` holds the ctypes front end (same names as the C entry points);
 ``workloads`` the seeded synthetic inputs.
@@ -16,6 +17,9 @@ from .binding import (  # noqa: F401
     attn_decode_paged_workspace_size,
     attn_kv_append,
     attn_prefill,
+    attn_qk_norm_rope,
+    attn_qk_norm_rope_append,
+    attn_rope_table,
     attn_status_string,
     load_library,
 )

@@ -50,6 +50,14 @@ def load_library():
     lib.attn_decode_paged.restype = I
     lib.attn_kv_append.argtypes = [P, P, P, P, P, I64, I, I, I, I64, P]
     lib.attn_kv_append.restype = I
+    F, D_ = ctypes.c_float, ctypes.c_double
+    lib.attn_rope_table.argtypes = [P, P, I, I, D_, P]
+    lib.attn_rope_table.restype = I
+    lib.attn_qk_norm_rope.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I, F, P]
+    lib.attn_qk_norm_rope.restype = I
+    lib.attn_qk_norm_rope_append.argtypes = [P, P, P, P, P, P, P, P, I64, I, I, I, I, F,
+                                             P, P, P, I, I64, P]
+    lib.attn_qk_norm_rope_append.restype = I
     _lib = lib
     return lib
 
@@ -161,3 +169,84 @@ def attn_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) ->
                                        _stream_handle(stream, k_new.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_kv_append")
+
+
+def attn_rope_table(cos_table, sin_table, theta: float, stream=None) -> None:
+    """Fill fp32 device tables [max_pos, head_dim/2] with cos/sin of
+    pos * theta^(-2i/head_dim) via ``attn_rope_table``."""
+    import torch
+    if cos_table.dim() != 2 or tuple(sin_table.shape) != tuple(cos_table.shape):
+        raise ValueError("tables must both be [max_pos, head_dim/2]")
+    c = _dev_tensor(cos_table, torch.float32, "cos_table")
+    s = _dev_tensor(sin_table, torch.float32, "sin_table")
+    max_pos, half = cos_table.shape
+    st = load_library().attn_rope_table(c, s, max_pos, 2 * half, float(theta),
+                                        _stream_handle(stream, cos_table.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_rope_table")
+
+
+def _rope_args(q, k, q_weight, k_weight, cos_table, sin_table, positions):
+    import torch
+    H_q, D = q.shape[-2], q.shape[-1]
+    H_kv = k.shape[-2]
+    num_tokens = q.numel() // (H_q * D)
+    if k.shape[-1] != D or k.numel() != num_tokens * H_kv * D or positions.numel() != num_tokens:
+        raise ValueError("q, k and positions disagree on num_tokens / head_dim")
+    if cos_table.dim() != 2 or cos_table.shape[1] != D // 2 or \
+            tuple(sin_table.shape) != tuple(cos_table.shape):
+        raise ValueError("tables must be [max_pos, head_dim/2]")
+    if (q_weight is None) != (k_weight is None):
+        raise ValueError("q_weight and k_weight must both be given or both be None")
+    ptrs = [_dev_tensor(q, torch.float16, "q"), _dev_tensor(k, torch.float16, "k")]
+    if q_weight is None:
+        ptrs += [ctypes.c_void_p(None), ctypes.c_void_p(None)]
+    else:
+        if q_weight.numel() != D or k_weight.numel() != D:
+            raise ValueError("weights must have head_dim elements")
+        ptrs += [_dev_tensor(q_weight, torch.float16, "q_weight"),
+                 _dev_tensor(k_weight, torch.float16, "k_weight")]
+    ptrs += [_dev_tensor(cos_table, torch.float32, "cos_table"),
+             _dev_tensor(sin_table, torch.float32, "sin_table"),
+             _dev_tensor(positions, torch.int32, "positions")]
+    return ptrs, num_tokens, H_q, H_kv, D, cos_table.shape[0]
+
+
+def attn_qk_norm_rope(q, k, q_weight, k_weight, cos_table, sin_table, positions, eps: float = 1e-6,
+                      stream=None) -> None:
+    """In place: per-head RMSNorm (weights [D] fp16, or both None) then the
+    NeoX rotation of q [..., H_q, D] and k [..., H_kv, D] at int32 positions
+    [num_tokens], via ``attn_qk_norm_rope``."""
+    ptrs, n, H_q, H_kv, D, max_pos = _rope_args(q, k, q_weight, k_weight, cos_table, sin_table,
+                                                positions)
+    st = load_library().attn_qk_norm_rope(*ptrs, n, H_q, H_kv, D, max_pos, float(eps),
+                                          _stream_handle(stream, q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_qk_norm_rope")
+
+
+def attn_qk_norm_rope_append(q, k, v, q_weight, k_weight, cos_table, sin_table, positions,
+                             k_cache, v_cache, slot_mapping, eps: float = 1e-6, stream=None) -> None:
+    """attn_qk_norm_rope, and in the same pass the rotated k rows and the v
+    rows [..., H_kv, D] go to the paged caches [num_blocks, H_kv, block_size, D]
+    at int64 slot_mapping [num_tokens] (-1 skipped), via
+    ``attn_qk_norm_rope_append``."""
+    import torch
+    ptrs, n, H_q, H_kv, D, max_pos = _rope_args(q, k, q_weight, k_weight, cos_table, sin_table,
+                                                positions)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must have k's shape")
+    num_blocks, H2, block_size, D2 = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or H2 != H_kv or D2 != D or \
+            slot_mapping.numel() != n:
+        raise ValueError("cache / slot_mapping shape mismatch")
+    vp = _dev_tensor(v, torch.float16, "v")
+    kc = _dev_tensor(k_cache, torch.float16, "k_cache")
+    vc = _dev_tensor(v_cache, torch.float16, "v_cache")
+    sm = _dev_tensor(slot_mapping, torch.int64, "slot_mapping")
+    args = ptrs[:2] + [vp] + ptrs[2:]
+    st = load_library().attn_qk_norm_rope_append(*args, n, H_q, H_kv, D, max_pos, float(eps), kc, vc,
+                                                 sm, block_size, num_blocks,
+                                                 _stream_handle(stream, q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_qk_norm_rope_append")

@@ -182,3 +182,87 @@ ATTN_EXPORT attn_status_t attn_kv_append(const void* k_new, const void* v_new, v
   const hipError_t e = attn::launch_kv_append(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
+
+ATTN_EXPORT attn_status_t attn_rope_table(float* cos_table, float* sin_table, int max_pos,
+                                          int head_dim, double theta, void* stream) {
+  if (!cos_table || !sin_table || max_pos <= 0 || head_dim <= 0 || (head_dim & 1) || !(theta > 0.0))
+    return ATTN_ERR_INVALID_ARG;
+  if (!aligned(cos_table, 16) || !aligned(sin_table, 16)) return ATTN_ERR_INVALID_ARG;
+  if (ceil_div64((int64_t)max_pos * (head_dim / 2), 256) > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  const hipError_t e = attn::launch_rope_table(cos_table, sin_table, max_pos, head_dim, theta,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+static attn_status_t qk_norm_rope_common(void* q, void* k, const void* v, const void* q_weight,
+                                         const void* k_weight, const float* cos_table,
+                                         const float* sin_table, const int32_t* positions,
+                                         int64_t num_tokens, int H_q, int H_kv, int head_dim,
+                                         int max_pos, float eps, void* k_cache, void* v_cache,
+                                         const int64_t* slot_mapping, int block_size,
+                                         int64_t num_blocks, bool append, void* stream) {
+  if (num_tokens < 0 || H_q <= 0 || H_kv <= 0 || head_dim <= 0 || max_pos <= 0 || !(eps >= 0.0f))
+    return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return ATTN_OK;  // nothing is read or written
+  if (!q || !k || !cos_table || !sin_table || !positions) return ATTN_ERR_INVALID_ARG;
+  if ((q_weight == nullptr) != (k_weight == nullptr)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(cos_table, 16) || !aligned(sin_table, 16) ||
+      !aligned(positions, 4) || (q_weight && (!aligned(q_weight, 16) || !aligned(k_weight, 16))))
+    return ATTN_ERR_INVALID_ARG;
+  if (append) {
+    if (!v || !k_cache || !v_cache || !slot_mapping || block_size <= 0 || num_blocks <= 0)
+      return ATTN_ERR_INVALID_ARG;
+    if (!aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+      return ATTN_ERR_INVALID_ARG;
+  }
+  const int64_t rows_per_block = (64 / (head_dim / 8)) * 4;
+  const int64_t heads = (int64_t)H_q + (int64_t)H_kv * (append ? 2 : 1);
+  if (num_tokens > ((int64_t)1 << 40) / heads ||
+      ceil_div64(num_tokens * heads, rows_per_block) > (int64_t)0x7fffffff)
+    return ATTN_ERR_UNSUPPORTED;
+  attn::RopeArgs a;
+  a.q = static_cast<_Float16*>(q);
+  a.k = static_cast<_Float16*>(k);
+  a.v = static_cast<const _Float16*>(v);
+  a.q_weight = static_cast<const _Float16*>(q_weight);
+  a.k_weight = static_cast<const _Float16*>(k_weight);
+  a.cos_table = cos_table;
+  a.sin_table = sin_table;
+  a.positions = positions;
+  a.k_cache = static_cast<_Float16*>(k_cache);
+  a.v_cache = static_cast<_Float16*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_blocks = append ? num_blocks : 0;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.max_pos = max_pos;
+  a.block_size = append ? block_size : 1;
+  a.eps = eps;
+  const hipError_t e = attn::launch_qk_norm_rope(a, head_dim, append, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_EXPORT attn_status_t attn_qk_norm_rope(void* q, void* k, const void* q_weight,
+                                            const void* k_weight, const float* cos_table,
+                                            const float* sin_table, const int32_t* positions,
+                                            int64_t num_tokens, int H_q, int H_kv, int head_dim,
+                                            int max_pos, float eps, void* stream) {
+  return qk_norm_rope_common(q, k, nullptr, q_weight, k_weight, cos_table, sin_table, positions,
+                             num_tokens, H_q, H_kv, head_dim, max_pos, eps, nullptr, nullptr,
+                             nullptr, 0, 0, false, stream);
+}
+
+ATTN_EXPORT attn_status_t attn_qk_norm_rope_append(void* q, void* k, const void* v,
+                                                   const void* q_weight, const void* k_weight,
+                                                   const float* cos_table, const float* sin_table,
+                                                   const int32_t* positions, int64_t num_tokens,
+                                                   int H_q, int H_kv, int head_dim, int max_pos,
+                                                   float eps, void* k_cache, void* v_cache,
+                                                   const int64_t* slot_mapping, int block_size,
+                                                   int64_t num_blocks, void* stream) {
+  return qk_norm_rope_common(q, k, v, q_weight, k_weight, cos_table, sin_table, positions,
+                             num_tokens, H_q, H_kv, head_dim, max_pos, eps, k_cache, v_cache,
+                             slot_mapping, block_size, num_blocks, true, stream);
+}

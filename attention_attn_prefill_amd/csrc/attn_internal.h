@@ -53,10 +53,31 @@ struct KvAppendArgs {
   int H_kv, head_dim, block_size;
 };
 
+struct RopeArgs {
+  _Float16* q;                 // [num_tokens, H_q, D], updated in place
+  _Float16* k;                 // [num_tokens, H_kv, D], updated in place
+  const _Float16* v;           // [num_tokens, H_kv, D] (append only)
+  const _Float16* q_weight;    // [D] or null (no norm)
+  const _Float16* k_weight;
+  const float* cos_table;      // [max_pos, D/2]
+  const float* sin_table;
+  const int32_t* positions;    // [num_tokens]
+  _Float16* k_cache;           // [num_blocks, H_kv, block_size, D] (append only)
+  _Float16* v_cache;
+  const int64_t* slot_mapping; // [num_tokens] (append only)
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int H_q, H_kv, max_pos, block_size;
+  float eps;
+};
+
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+hipError_t launch_qk_norm_rope(const RopeArgs& a, int head_dim, bool append, hipStream_t stream);
+hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_pos, int head_dim, double theta,
+                             hipStream_t stream);
 
 // Decode split policy (shared by the workspace-size query and the launch).
 constexpr int kDecodeBlockSize = 16;

@@ -2,7 +2,7 @@
  * attn.h -- C ABI of libattn.so: scaled-dot-product attention with online
  * softmax on AMD Instinct MI355X (gfx950).
  *
- * Two operations, both from "Tutorial: Adding a New Kernel to RL.cu"
+ * The attention operations come from "Tutorial: Adding a New Kernel to RL.cu"
  * (skillsmp.com add-cuda-kernel page), attention.cuh listing:
  *   - attn_prefill: causal (or non-causal) GQA prefill, the "Flash Attention 2
  *     -- Prefill" section of that header;
@@ -11,6 +11,8 @@
  *     flash-decoding (named as the next step in the "Remaining Gap vs
  *     nano-vllm" section of the GRPO-CUDA project memory page) with a
  *     log-sum-exp merge.
+ * The cache append and the QK-norm + rotary step around them follow the
+ * GRPO-CUDA project memory page (sections cited at each declaration).
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers (HIP device memory or memory the device can
@@ -149,6 +151,70 @@ attn_status_t attn_kv_append(const void* k_new, const void* v_new,
                              const int64_t* slot_mapping, int64_t num_tokens,
                              int H_kv, int head_dim, int block_size,
                              int64_t num_blocks, void* stream);
+
+/*
+ * RoPE table: fill the fp32 tables the rotation reads ("GRPO-CUDA Project
+ * Memory" page, "RoPE design": NeoX split-half, table [max_seq_len, D/2]
+ * precomputed once).  Pair i of a head at position p turns by the angle
+ * p * theta^(-2i/D):
+ *
+ *   cos_table[p * (head_dim/2) + i] = cos(p * theta^(-2i/head_dim))
+ *   sin_table[p * (head_dim/2) + i] = sin(...)           p < max_pos
+ *
+ * theta is the model's rotary base (not on the pages; Qwen3 configurations
+ * use 1e6).  The angle, cosine and sine are evaluated in fp64 and rounded to
+ * fp32 once.  head_dim must be even and positive; tables 16-byte aligned.
+ */
+attn_status_t attn_rope_table(float* cos_table, float* sin_table, int max_pos,
+                              int head_dim, double theta, void* stream);
+
+/*
+ * QK-norm + rotary embedding, in place (the Qwen3 order: RMSNorm on every
+ * query and key head, then the NeoX rotation; "GRPO-CUDA Project Memory"
+ * page, "Qwen3 key dims", "Qwen3-Specific Notes" and "RoPE design").
+ *
+ *   q         [num_tokens, H_q, head_dim] fp16 (updated)
+ *   k         [num_tokens, H_kv, head_dim] fp16 (updated)
+ *   q_weight, k_weight  [head_dim] fp16 RMSNorm weights, or NULL for the
+ *             rotation only (both NULL or both set)
+ *   cos_table, sin_table  [max_pos, head_dim/2] fp32 (attn_rope_table)
+ *   positions [num_tokens] int32: the token's position in its sequence
+ *
+ * Per head: y_d = x_d / sqrt(mean_e x_e^2 + eps) * w_d, then for
+ * i < D/2: out_i = y_i cos - y_{i+D/2} sin, out_{i+D/2} = y_{i+D/2} cos +
+ * y_i sin, with the position's table entries.  fp32 throughout, one
+ * rounding to fp16 at the end.  head_dim: 32, 64 or 128.  A [B, S, H, D]
+ * prefill tensor is num_tokens = B*S.  num_tokens == 0 is a no-op (the
+ * pointers are then not checked).
+ * Device-side precondition: 0 <= positions[t] < max_pos; a token that
+ * breaks it gets NaN in all of its q and k rows (no out-of-bounds access).
+ */
+attn_status_t attn_qk_norm_rope(void* q, void* k, const void* q_weight,
+                                const void* k_weight, const float* cos_table,
+                                const float* sin_table, const int32_t* positions,
+                                int64_t num_tokens, int H_q, int H_kv,
+                                int head_dim, int max_pos, float eps,
+                                void* stream);
+
+/*
+ * attn_qk_norm_rope fused with the paged KV append: as above, and in the
+ * same pass every token's rotated key rows and its value rows
+ * v [num_tokens, H_kv, head_dim] fp16 (read only) are written to
+ * k_cache / v_cache [num_blocks, H_kv, block_size, head_dim] at
+ * slot_mapping[t] (int64; slots outside [0, num_blocks * block_size),
+ * -1 included, are skipped), exactly as attn_kv_append places them.  This is
+ * the step between the projections and attention in the pages' Qwen3 layer
+ * order ("QK-norm -> RoPE -> KV append -> attn").  A token with a bad
+ * position writes NaN key rows to its slot.
+ */
+attn_status_t attn_qk_norm_rope_append(void* q, void* k, const void* v,
+                                       const void* q_weight, const void* k_weight,
+                                       const float* cos_table, const float* sin_table,
+                                       const int32_t* positions, int64_t num_tokens,
+                                       int H_q, int H_kv, int head_dim, int max_pos,
+                                       float eps, void* k_cache, void* v_cache,
+                                       const int64_t* slot_mapping, int block_size,
+                                       int64_t num_blocks, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

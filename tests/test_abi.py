@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "attn_abi_version", "attn_status_string", "attn_prefill",
-        "attn_decode_paged_workspace_size", "attn_decode_paged", "attn_kv_append"])
+        "attn_decode_paged_workspace_size", "attn_decode_paged", "attn_kv_append",
+        "attn_rope_table", "attn_qk_norm_rope", "attn_qk_norm_rope_append"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -136,3 +137,51 @@ def append(lib, kn=P, vn=P, kc=P2, vc=P2, sm=P, n=16, H_kv=8, D=128, bs=16, nb=4
 ])
 def test_kv_append_rejects(lib, kw, want):
     assert append(lib, **kw) == want
+
+
+def rope_table(lib, c=P, s=P2, max_pos=64, D=128, theta=1e6):
+    return lib.attn_rope_table(c, s, max_pos, D, theta, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(c=NULL), INV), (dict(s=NULL), INV), (dict(max_pos=0), INV), (dict(D=0), INV),
+    (dict(D=7), INV), (dict(theta=0.0), INV), (dict(theta=-1.0), INV),
+    (dict(c=ctypes.c_void_p(0x10004)), INV),
+])
+def test_rope_table_rejects(lib, kw, want):
+    assert rope_table(lib, **kw) == want
+
+
+def qk_rope(lib, q=P, k=P2, qw=P, kw_=P2, c=P, s=P2, pos=P, n=16, H_q=16, H_kv=8, D=128,
+            max_pos=64, eps=1e-6):
+    return lib.attn_qk_norm_rope(q, k, qw, kw_, c, s, pos, n, H_q, H_kv, D, max_pos, eps, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), INV), (dict(k=NULL), INV), (dict(c=NULL), INV), (dict(s=NULL), INV),
+    (dict(pos=NULL), INV), (dict(qw=NULL), INV), (dict(kw_=NULL), INV),
+    (dict(n=-1), INV), (dict(H_q=0), INV), (dict(H_kv=0), INV), (dict(max_pos=0), INV),
+    (dict(eps=-1e-6), INV), (dict(eps=float("nan")), INV), (dict(D=0), INV),
+    (dict(D=96), UNS), (dict(D=256), UNS),
+    (dict(q=ctypes.c_void_p(0x10008)), INV), (dict(pos=ctypes.c_void_p(0x10002)), INV),
+    (dict(qw=ctypes.c_void_p(0x10008)), INV),
+    (dict(n=0), OK), (dict(n=0, qw=NULL, kw_=NULL), OK), (dict(n=0, q=NULL, pos=NULL), OK),
+    (dict(n=0, D=96), UNS), (dict(n=0, H_q=0), INV),
+])
+def test_qk_norm_rope_rejects(lib, kw, want):
+    assert qk_rope(lib, **kw) == want
+
+
+def qk_rope_append(lib, v=P, kc=P2, vc=P2, sm=P, bs=16, nb=4, n=16, D=128):
+    return lib.attn_qk_norm_rope_append(P, P2, v, P, P2, P, P2, P, n, 16, 8, D, 64, 1e-6, kc, vc, sm,
+                                        bs, nb, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(v=NULL), INV), (dict(kc=NULL), INV), (dict(vc=NULL), INV), (dict(sm=NULL), INV),
+    (dict(bs=0), INV), (dict(nb=0), INV), (dict(D=64 + 8), UNS),
+    (dict(sm=ctypes.c_void_p(0x10004)), INV), (dict(v=ctypes.c_void_p(0x10008)), INV),
+    (dict(n=0), OK),
+])
+def test_qk_norm_rope_append_rejects(lib, kw, want):
+    assert qk_rope_append(lib, **kw) == want
