@@ -156,6 +156,59 @@ def time_kv_append(pcfg, k, v, dev, stream, W, iters=100):
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, iters=100):
+    """The Qwen3 step between the projections and attention on the prefill's
+    B*S tokens: QK RMSNorm + NeoX RoPE in place, fused with the paged append
+    of the rotated K and of V (theta 1e6, positions 0..S-1 per sequence).
+    Algorithmic HBM bytes: q and k read and written, v read, the cache rows
+    of k and v written, one table row (cos + sin) per token, the position
+    and slot of every token."""
+    import torch
+
+    from attention_attn_prefill_amd import attn_qk_norm_rope_append, attn_rope_table
+    n, D = pcfg.B * pcfg.S_q, pcfg.D
+    lens = [pcfg.S_kv] * pcfg.B
+    bt, nb = W.paged_layout(lens, 16, (pcfg.S_kv + 15) // 16, (12, 12))
+    slots = np.concatenate([bt[s, np.arange(L) // 16].astype(np.int64) * 16 + np.arange(L) % 16
+                            for s, L in enumerate(lens)])
+    tq = torch.from_numpy(q).to(dev).view(n, pcfg.H_q, D)
+    tk = torch.from_numpy(k).to(dev).view(n, pcfg.H_kv, D)
+    tv = torch.from_numpy(v).to(dev).view(n, pcfg.H_kv, D)
+    kc = torch.empty((nb, pcfg.H_kv, 16, D), dtype=torch.float16, device=dev)
+    vc = torch.empty_like(kc)
+    sm = torch.from_numpy(slots).to(dev)
+    pos = torch.arange(pcfg.S_q, dtype=torch.int32, device=dev).repeat(pcfg.B)
+    rng = np.random.default_rng(13)
+    qw = torch.from_numpy(rng.uniform(0.25, 2.0, D).astype(np.float16)).to(dev)
+    kw = torch.from_numpy(rng.uniform(0.25, 2.0, D).astype(np.float16)).to(dev)
+    max_pos = 40960
+    ct = torch.empty((max_pos, D // 2), dtype=torch.float32, device=dev)
+    st = torch.empty_like(ct)
+    attn_rope_table(ct, st, 1e6, stream=stream)
+
+    def run():
+        attn_qk_norm_rope_append(tq, tk, tv, qw, kw, ct, st, pos, kc, vc, sm, stream=stream)
+
+    for _ in range(20):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    row = D * 2
+    nbytes = (2 * n * pcfg.H_q * row + 2 * n * pcfg.H_kv * row + n * pcfg.H_kv * row
+              + 2 * n * pcfg.H_kv * row + n * D * 4 + n * 4 + n * 8)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "QK-norm + RoPE + paged append GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "tokens": n, "bytes": int(nbytes), "launch_ms": round(ms, 5),
+            "roofline": {"bound": "hbm", "kernel": "qk_norm_rope_kernel<128,append>",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -276,6 +329,7 @@ def main():
         },
     }
     line["kv_append"] = time_kv_append(pcfg, k, v, dev, stream, W)
+    line["qk_norm_rope_append"] = time_qk_norm_rope(pcfg, q, k, v, dev, stream, W)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl,
