@@ -67,6 +67,8 @@ class Oracle:
         lib.oracle_rope_table.restype = I
         lib.oracle_qk_norm_rope.argtypes = [P, P, P, P, P, I64, I, I, I, D_, P]
         lib.oracle_qk_norm_rope.restype = I
+        lib.oracle_cross_attention.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D_, P]
+        lib.oracle_cross_attention.restype = I
         self._lib = lib
         return lib
 
@@ -194,6 +196,23 @@ class Oracle:
             raise ValueError("oracle_qk_norm_rope rejected its arguments")
         return out
 
+    def cross_attention(self, x_q, x_kv, w_q, w_k, w_v, w_o, H: int, base: float = 10000.0):
+        """The cross-attention module with interleaved-pair RoPE: x_q
+        [B,T_q,dim], x_kv [B,T_k,dim], weights [dim,dim] (nn.Linear [out,in]),
+        all float16.  Returns float64 [B,T_q,dim]."""
+        x_q, x_kv = _f16(x_q), _f16(x_kv)
+        ws = [_f16(w) for w in (w_q, w_k, w_v, w_o)]
+        B, T_q, dim = x_q.shape
+        Bk, T_k, dimk = x_kv.shape
+        if Bk != B or dimk != dim or any(w.shape != (dim, dim) for w in ws):
+            raise ValueError("shape mismatch")
+        out = np.empty((B, T_q, dim), np.float64)
+        rc = self._load().oracle_cross_attention(_ptr(x_q), _ptr(x_kv), *[_ptr(w) for w in ws], B, T_q,
+                                                 T_k, dim, int(H), float(base), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_cross_attention rejected its arguments")
+        return out
+
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
@@ -214,3 +233,4 @@ decode_paged = default.decode_paged
 kv_append = default.kv_append
 rope_table = default.rope_table
 qk_norm_rope = default.qk_norm_rope
+cross_attention = default.cross_attention

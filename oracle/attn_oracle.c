@@ -392,3 +392,120 @@ int oracle_qk_norm_rope(const uint16_t* x, const uint16_t* weight, const int32_t
   free(y);
   return 0;
 }
+
+/* ---- cross-attention module with RoPE --------------------------------------- */
+/* The module of the cross-attention trace (POPCORNBENCH "Kimi-K2.6" page, the
+ * problem statement and its nn.Linear notes): one layer of multi-head
+ * cross-attention with rotary embeddings, no bias anywhere, dropout p = 0.
+ *   Q = x_q W_q^T   [B, T_q, dim]     K = x_kv W_k^T, V = x_kv W_v^T [B, T_k, dim]
+ *   head h is columns h*D .. h*D+D-1 (D = dim / H)
+ *   RoPE on Q and K, adjacent pairs (2j, 2j+1) turned by pos * base^(-2j/D),
+ *     pos = the row's index in its sequence (0..T-1):
+ *       r_{2j}   = u_{2j} cos - u_{2j+1} sin
+ *       r_{2j+1} = u_{2j} sin + u_{2j+1} cos
+ *   A_h = softmax(Q_h K_h^T / sqrt(D)) V_h     (no mask)
+ *   out = concat_h(A_h) W_o^T   [B, T_q, dim]
+ * x_q, x_kv and the four [dim, dim] weights (nn.Linear layout [out, in]) are
+ * binary16; every intermediate here is fp64.
+ * Returns 0, or -1 on invalid arguments.                                     */
+int oracle_cross_attention(const uint16_t* x_q, const uint16_t* x_kv, const uint16_t* w_q,
+                           const uint16_t* w_k, const uint16_t* w_v, const uint16_t* w_o,
+                           int B, int T_q, int T_k, int dim, int H, double base, double* out) {
+  if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !out) return -1;
+  if (B <= 0 || T_q <= 0 || T_k <= 0 || dim <= 0 || H <= 0 || dim % H || ((dim / H) & 1) ||
+      !(base > 0.0))
+    return -1;
+  const int D = dim / H;
+  const int64_t nq = (int64_t)B * T_q, nk = (int64_t)B * T_k;
+  double* Q = (double*)malloc(sizeof(double) * nq * dim);
+  double* K = (double*)malloc(sizeof(double) * nk * dim);
+  double* V = (double*)malloc(sizeof(double) * nk * dim);
+  double* A = (double*)malloc(sizeof(double) * nq * dim);
+  if (!Q || !K || !V || !A) {
+    free(Q); free(K); free(V); free(A);
+    return -1;
+  }
+  /* projections: y[r][c] = sum_e x[r][e] * W[c][e] */
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < nq + nk; ++r) {
+    for (int c = 0; c < dim; ++c) {
+      if (r < nq) {
+        double s = 0.0;
+        for (int e = 0; e < dim; ++e)
+          s += half_bits_to_double(x_q[r * dim + e]) * half_bits_to_double(w_q[(int64_t)c * dim + e]);
+        Q[r * dim + c] = s;
+      } else {
+        const int64_t rk = r - nq;
+        double sk = 0.0, sv = 0.0;
+        for (int e = 0; e < dim; ++e) {
+          const double xe = half_bits_to_double(x_kv[rk * dim + e]);
+          sk += xe * half_bits_to_double(w_k[(int64_t)c * dim + e]);
+          sv += xe * half_bits_to_double(w_v[(int64_t)c * dim + e]);
+        }
+        K[rk * dim + c] = sk;
+        V[rk * dim + c] = sv;
+      }
+    }
+  }
+  /* rotary embedding on Q (positions 0..T_q-1) and K (0..T_k-1) */
+  for (int which = 0; which < 2; ++which) {
+    double* X = which ? K : Q;
+    const int T = which ? T_k : T_q;
+    const int64_t rows = which ? nk : nq;
+    for (int64_t r = 0; r < rows; ++r) {
+      const double pos = (double)(r % T);
+      for (int h = 0; h < H; ++h) {
+        double* u = X + r * dim + (int64_t)h * D;
+        for (int j = 0; j < D / 2; ++j) {
+          const double ang = pos * pow(base, -2.0 * (double)j / (double)D);
+          const double c = cos(ang), s = sin(ang);
+          const double a = u[2 * j], b = u[2 * j + 1];
+          u[2 * j] = a * c - b * s;
+          u[2 * j + 1] = a * s + b * c;
+        }
+      }
+    }
+  }
+  /* attention per (batch, head, query row), no mask */
+  const double scale = pow((double)D, -0.5);
+#pragma omp parallel for schedule(static)
+  for (int64_t qi = 0; qi < nq * H; ++qi) {
+    const int64_t r = qi / H;
+    const int h = (int)(qi % H);
+    const int64_t b = r / T_q;
+    double* sc = (double*)malloc(sizeof(double) * T_k);
+    const double* q = Q + r * dim + (int64_t)h * D;
+    double m = -INFINITY;
+    for (int j = 0; j < T_k; ++j) {
+      const double* k = K + (b * T_k + j) * dim + (int64_t)h * D;
+      double s = 0.0;
+      for (int d = 0; d < D; ++d) s += q[d] * k[d];
+      sc[j] = s * scale;
+      if (sc[j] > m) m = sc[j];
+    }
+    double z = 0.0;
+    for (int j = 0; j < T_k; ++j) {
+      sc[j] = exp(sc[j] - m);
+      z += sc[j];
+    }
+    double* a = A + r * dim + (int64_t)h * D;
+    for (int d = 0; d < D; ++d) a[d] = 0.0;
+    for (int j = 0; j < T_k; ++j) {
+      const double* v = V + (b * T_k + j) * dim + (int64_t)h * D;
+      const double p = sc[j] / z;
+      for (int d = 0; d < D; ++d) a[d] += p * v[d];
+    }
+    free(sc);
+  }
+  /* output projection */
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < nq; ++r) {
+    for (int c = 0; c < dim; ++c) {
+      double s = 0.0;
+      for (int e = 0; e < dim; ++e) s += A[r * dim + e] * half_bits_to_double(w_o[(int64_t)c * dim + e]);
+      out[r * dim + c] = s;
+    }
+  }
+  free(Q); free(K); free(V); free(A);
+  return 0;
+}

@@ -33,6 +33,8 @@ What pins what:
   * QK RMSNorm               -- unit mean square, scale invariance, a
                                 constant-row closed form (mean, eps, weight);
                                 numpy RMSNorm then rotation (the pages' order)
+  * cross-attention module   -- torch fp64 (F.linear, complex RoPE, SDPA);
+                                identical memory rows; a single key
 """
 from __future__ import annotations
 
@@ -529,6 +531,72 @@ def pin_rope_rejects_invalid(ora):
         except ValueError:
             continue
         raise AssertionError(f"rope_table accepted {args}")
+
+
+# ---- cross-attention module with interleaved-pair RoPE ------------------------
+
+def _module_inputs(B, T_q, T_k, dim, seed):
+    rng = np.random.default_rng(seed)
+    xq = rng.standard_normal((B, T_q, dim)).astype(np.float16)
+    xk = rng.standard_normal((B, T_k, dim)).astype(np.float16)
+    bound = 1.0 / math.sqrt(dim)
+    ws = [rng.uniform(-bound, bound, (dim, dim)).astype(np.float16) for _ in range(4)]
+    return xq, xk, ws
+
+
+def _torch_module(xq, xk, ws, H, base):
+    """The module written with torch in fp64 on the CPU: F.linear, RoPE as a
+    complex product over adjacent pairs (torch.view_as_complex / torch.polar),
+    scaled_dot_product_attention, F.linear."""
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: torch.from_numpy(_f64(a))
+    B, T_q, dim = xq.shape
+    T_k, D = xk.shape[1], dim // H
+    q, k, v = F.linear(t(xq), t(ws[0])), F.linear(t(xk), t(ws[1])), F.linear(t(xk), t(ws[2]))
+
+    def rope(x, T):
+        x = x.view(B, T, H, D // 2, 2)
+        freq = base ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+        ang = torch.arange(T, dtype=torch.float64)[:, None] * freq[None, :]
+        z = torch.view_as_complex(x.contiguous()) * torch.polar(torch.ones_like(ang), ang)[None, :, None, :]
+        return torch.view_as_real(z).reshape(B, T, H, D)
+
+    qh = rope(q, T_q).transpose(1, 2).contiguous()
+    kh = rope(k, T_k).transpose(1, 2).contiguous()
+    vh = v.view(B, T_k, H, D).transpose(1, 2).contiguous()
+    a = F.scaled_dot_product_attention(qh, kh, vh)
+    return F.linear(a.transpose(1, 2).reshape(B, T_q, dim), t(ws[3])).numpy()
+
+
+def pin_cross_attention_matches_torch(ora):
+    """The pages' shape (B=4, T_q=64, T_k=128, dim=256, 8 heads) and two
+    others, against the torch fp64 module."""
+    for (B, T_q, T_k, dim, H, base, seed) in ((4, 64, 128, 256, 8, 1e4, 301), (2, 5, 9, 64, 2, 1e4, 302),
+                                              (1, 17, 3, 128, 1, 5e5, 303)):
+        xq, xk, ws = _module_inputs(B, T_q, T_k, dim, seed)
+        got = ora.cross_attention(xq, xk, *ws, H=H, base=base)
+        assert np.allclose(got, _torch_module(xq, xk, ws, H, base), rtol=1e-12, atol=1e-13), (B, T_q, T_k, dim, H)
+
+
+def pin_cross_attention_identical_memory_rows(ora):
+    """Identical x_kv rows give identical value rows: every query attends to
+    the same value whatever the softmax weights, so out = (x W_v^T) W_o^T."""
+    B, T_q, T_k, dim, H = 2, 7, 11, 64, 4
+    xq, xk, ws = _module_inputs(B, T_q, T_k, dim, 304)
+    xk[:] = xk[:, :1, :]
+    got = ora.cross_attention(xq, xk, *ws, H=H)
+    want = (_f64(xk[:, 0]) @ _f64(ws[2]).T) @ _f64(ws[3]).T
+    assert np.allclose(got, np.broadcast_to(want[:, None, :], got.shape), rtol=1e-12, atol=1e-14)
+
+
+def pin_cross_attention_single_key(ora):
+    """With one key the softmax is 1 and RoPE on K is the identity (pos 0)."""
+    B, T_q, dim, H = 3, 6, 32, 2
+    xq, xk, ws = _module_inputs(B, T_q, 1, dim, 305)
+    got = ora.cross_attention(xq, xk, *ws, H=H)
+    want = (_f64(xk[:, 0]) @ _f64(ws[2]).T) @ _f64(ws[3]).T
+    assert np.allclose(got, np.broadcast_to(want[:, None, :], got.shape), rtol=1e-12, atol=1e-14)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -49,6 +49,16 @@ MUTANTS = [
     ("rmsnorm: eps outside the root", "sqrt(ss / (double)D + eps)", "(sqrt(ss / (double)D) + eps)"),
     ("rmsnorm: sum instead of mean", "sqrt(ss / (double)D + eps)", "sqrt(ss + eps)"),
     ("rmsnorm: weight dropped", "y[d] = y[d] / r * half_bits_to_double(weight[d]);", "y[d] = y[d] / r;"),
+    ("module: NeoX pairs instead of adjacent ones", "const double a = u[2 * j], b = u[2 * j + 1];",
+     "const double a = u[j], b = u[j + D / 2];"),
+    ("module: x W instead of x W^T", "half_bits_to_double(w_q[(int64_t)c * dim + e])",
+     "half_bits_to_double(w_q[(int64_t)e * dim + c])"),
+    ("module: key positions shifted by one", "const double pos = (double)(r % T);",
+     "const double pos = (double)(r % T + which);"),
+    ("module: scale 1/D", "const double scale = pow((double)D, -0.5);", "const double scale = pow((double)D, -1.0);"),
+    ("module: output projection skipped", "out[r * dim + c] = s;", "out[r * dim + c] = A[r * dim + c];"),
+    ("module: value projection with W_k", "sv += xe * half_bits_to_double(w_v[(int64_t)c * dim + e]);",
+     "sv += xe * half_bits_to_double(w_k[(int64_t)c * dim + e]);"),
     ("rmsnorm: weight reversed", "y[d] = y[d] / r * half_bits_to_double(weight[d]);",
      "y[d] = y[d] / r * half_bits_to_double(weight[D - 1 - d]);"),
 ]
