@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     ATTN_OK,
     AttnError,
     attn_abi_version,
+    attn_cross_attention,
+    attn_cross_attention_workspace_size,
     attn_decode_paged,
     attn_decode_paged_workspace_size,
     attn_kv_append,

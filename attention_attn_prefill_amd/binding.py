@@ -58,6 +58,10 @@ def load_library():
     lib.attn_qk_norm_rope_append.argtypes = [P, P, P, P, P, P, P, P, I64, I, I, I, I, F,
                                              P, P, P, I, I64, P]
     lib.attn_qk_norm_rope_append.restype = I
+    lib.attn_cross_attention_workspace_size.argtypes = [I, I, I, I, I]
+    lib.attn_cross_attention_workspace_size.restype = SZ
+    lib.attn_cross_attention.argtypes = [P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, P, SZ, P]
+    lib.attn_cross_attention.restype = I
     _lib = lib
     return lib
 
@@ -250,3 +254,34 @@ def attn_qk_norm_rope_append(q, k, v, q_weight, k_weight, cos_table, sin_table, 
                                                  _stream_handle(stream, q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_qk_norm_rope_append")
+
+
+def attn_cross_attention_workspace_size(B: int, T_q: int, T_k: int, dim: int, H: int) -> int:
+    return int(load_library().attn_cross_attention_workspace_size(B, T_q, T_k, dim, H))
+
+
+def attn_cross_attention(x_q, x_kv, w_q, w_k, w_v, w_o, cos_table, sin_table, out, H: int,
+                         workspace, stream=None) -> None:
+    """The cross-attention module with adjacent-pair RoPE via
+    ``attn_cross_attention``: x_q [B,T_q,dim], x_kv [B,T_k,dim], weights
+    [dim,dim] fp16 (nn.Linear [out,in]); fp32 tables [max_pos, dim/H/2];
+    out [B,T_q,dim] fp16; workspace a uint8 device tensor of at least
+    ``attn_cross_attention_workspace_size`` bytes."""
+    import torch
+    B, T_q, dim = x_q.shape
+    B2, T_k, dim2 = x_kv.shape
+    if B2 != B or dim2 != dim or tuple(out.shape) != tuple(x_q.shape) or \
+            any(tuple(w.shape) != (dim, dim) for w in (w_q, w_k, w_v, w_o)):
+        raise ValueError("shape mismatch")
+    if cos_table.dim() != 2 or tuple(sin_table.shape) != tuple(cos_table.shape):
+        raise ValueError("tables must be [max_pos, head_dim/2]")
+    ptrs = [_dev_tensor(t, torch.float16, n) for t, n in ((x_q, "x_q"), (x_kv, "x_kv"), (w_q, "w_q"),
+                                                          (w_k, "w_k"), (w_v, "w_v"), (w_o, "w_o"))]
+    ptrs += [_dev_tensor(cos_table, torch.float32, "cos_table"),
+             _dev_tensor(sin_table, torch.float32, "sin_table")]
+    ws = _dev_tensor(workspace, torch.uint8, "workspace")
+    st = load_library().attn_cross_attention(*ptrs, cos_table.shape[0], _dev_tensor(out, torch.float16, "out"),
+                                             B, T_q, T_k, dim, int(H), ws, workspace.numel(),
+                                             _stream_handle(stream, x_q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_cross_attention")

@@ -266,3 +266,97 @@ ATTN_EXPORT attn_status_t attn_qk_norm_rope_append(void* q, void* k, const void*
                              num_tokens, H_q, H_kv, head_dim, max_pos, eps, k_cache, v_cache,
                              slot_mapping, block_size, num_blocks, true, stream);
 }
+
+// ---- cross-attention module ------------------------------------------------
+// Workspace: q [B*T_q, dim], k and v [B*T_k, dim], the attention output
+// [B*T_q, dim], fp16, each part 256-byte aligned.
+static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+static attn_status_t check_cross(int B, int T_q, int T_k, int dim, int H) {
+  if (B <= 0 || T_q <= 0 || T_k <= 0 || dim <= 0 || H <= 0 || dim % H) return ATTN_ERR_INVALID_ARG;
+  const int D = dim / H;
+  if (D != 32 && D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dim % 32) return ATTN_ERR_UNSUPPORTED;
+  // every operand below 2 GiB (32-bit buffer offsets), also per batch entry for attention
+  const int64_t rows = (int64_t)B * (T_q > T_k ? T_q : T_k);
+  if (rows * dim * 2 >= ((int64_t)1 << 31) || (int64_t)dim * dim * 2 >= ((int64_t)1 << 31))
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+static int64_t cross_ws_bytes(int B, int T_q, int T_k, int dim) {
+  const int64_t q = align256((int64_t)B * T_q * dim * 2);
+  const int64_t kv = align256((int64_t)B * T_k * dim * 2);
+  return 2 * q + 2 * kv;
+}
+
+ATTN_EXPORT size_t attn_cross_attention_workspace_size(int B, int T_q, int T_k, int dim, int H) {
+  if (check_cross(B, T_q, T_k, dim, H) != ATTN_OK) return 0;
+  return (size_t)cross_ws_bytes(B, T_q, T_k, dim);
+}
+
+ATTN_EXPORT attn_status_t attn_cross_attention(const void* x_q, const void* x_kv, const void* w_q,
+                                               const void* w_k, const void* w_v, const void* w_o,
+                                               const float* cos_table, const float* sin_table,
+                                               int max_pos, void* out, int B, int T_q, int T_k,
+                                               int dim, int H, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !cos_table || !sin_table || !out)
+    return ATTN_ERR_INVALID_ARG;
+  const attn_status_t st = check_cross(B, T_q, T_k, dim, H);
+  if (st != ATTN_OK) return st;
+  if (max_pos < T_q || max_pos < T_k) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(x_q, 16) || !aligned(x_kv, 16) || !aligned(w_q, 16) || !aligned(w_k, 16) ||
+      !aligned(w_v, 16) || !aligned(w_o, 16) || !aligned(out, 16) || !aligned(cos_table, 4) ||
+      !aligned(sin_table, 4))
+    return ATTN_ERR_INVALID_ARG;
+  const int64_t need = cross_ws_bytes(B, T_q, T_k, dim);
+  if (!workspace || (int64_t)workspace_bytes < need || !aligned(workspace, 256)) return ATTN_ERR_WORKSPACE;
+  const int D = dim / H;
+  char* ws = static_cast<char*>(workspace);
+  const int64_t qb = align256((int64_t)B * T_q * dim * 2), kvb = align256((int64_t)B * T_k * dim * 2);
+  _Float16* q = reinterpret_cast<_Float16*>(ws);
+  _Float16* k = reinterpret_cast<_Float16*>(ws + qb);
+  _Float16* v = reinterpret_cast<_Float16*>(ws + qb + kvb);
+  _Float16* att = reinterpret_cast<_Float16*>(ws + qb + 2 * kvb);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const int64_t col_tiles = dim / 32;
+  attn::ProjArgs p{};
+  p.K = dim;
+  p.N = dim;
+  p.head_dim = D;
+  p.cos_table = cos_table;
+  p.sin_table = sin_table;
+  p.n_jobs = 3;
+  p.job[0] = {static_cast<const _Float16*>(x_q), static_cast<const _Float16*>(w_q), q, B * T_q, T_q, 1,
+              ceil_div64((int64_t)B * T_q, 32) * col_tiles};
+  p.job[1] = {static_cast<const _Float16*>(x_kv), static_cast<const _Float16*>(w_k), k, B * T_k, T_k, 1,
+              ceil_div64((int64_t)B * T_k, 32) * col_tiles};
+  p.job[2] = {static_cast<const _Float16*>(x_kv), static_cast<const _Float16*>(w_v), v, B * T_k, T_k, 0,
+              ceil_div64((int64_t)B * T_k, 32) * col_tiles};
+  if (attn::launch_proj(p, s) != hipSuccess) return ATTN_ERR_LAUNCH;
+
+  attn::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = att;
+  a.B = B;
+  a.S_q = T_q;
+  a.S_kv = T_k;
+  a.H_q = H;
+  a.H_kv = H;
+  a.n_qtiles = 0;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  if (attn::launch_prefill(a, D, false, s) != hipSuccess) return ATTN_ERR_LAUNCH;
+
+  attn::ProjArgs po{};
+  po.K = dim;
+  po.N = dim;
+  po.head_dim = D;
+  po.n_jobs = 1;
+  po.job[0] = {att, static_cast<const _Float16*>(w_o), static_cast<_Float16*>(out), B * T_q, T_q, 0,
+               ceil_div64((int64_t)B * T_q, 32) * col_tiles};
+  return attn::launch_proj(po, s) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

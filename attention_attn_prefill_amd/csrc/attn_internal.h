@@ -71,11 +71,29 @@ struct RopeArgs {
   float eps;
 };
 
+// One matrix of a projection launch: y[M, N] = x[M, K] w[N, K]^T, with the
+// adjacent-pair rotary epilogue when rope != 0 (position = row % T).
+struct ProjJob {
+  const _Float16* x;
+  const _Float16* w;
+  _Float16* y;
+  int M, T, rope;
+  int64_t tiles;  // (ceil(M / 32)) * (N / 32)
+};
+struct ProjArgs {
+  ProjJob job[3];
+  int n_jobs;
+  int K, N, head_dim;
+  const float* cos_table;  // [max_pos, head_dim / 2]
+  const float* sin_table;
+};
+
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_qk_norm_rope(const RopeArgs& a, int head_dim, bool append, hipStream_t stream);
+hipError_t launch_proj(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_pos, int head_dim, double theta,
                              hipStream_t stream);
 

@@ -14,11 +14,10 @@ Recipe:
     ``num_blocks = sum(ceil(L/16))``; physical ids are a seeded permutation of
     ``0..num_blocks-1`` handed out in (sequence, logical block) order; unused
     table entries are -1.
-  * the cross-attention workload's Q and K are rotated by interleaved-pair
-    rotary embeddings (pair (2j, 2j+1) turned by ``pos * base**(-2j/D)``,
-    positions 0..T-1, base 10000) in fp64 on the host, then rounded to
-    binary16 -- the convention of the POPCORNBENCH Kimi-K2.6 trace page
-    (its RoPE discussion).  This is input preparation, not part of the path.
+  * the cross-attention attention core (cross_attn) takes plain normal
+    Q/K/V; the rotary embedding of that workload belongs to the module
+    (x_q, x_kv and nn.Linear-style uniform weights from
+    ``cross_module_inputs``), which each side rotates with its own code.
   * the pages' own unit-test inputs ("Tutorial: Adding a New Kernel to
     RL.cu", test_attention.cu: the deterministic LCG helper and the test
     runners) are reproduced by ``pages_prefill_case`` / ``pages_decode_case``.
@@ -44,7 +43,6 @@ class PrefillConfig:
     H_kv: int
     D: int
     causal: bool
-    rope_base: float | None = None
 
     @property
     def pairs(self) -> int:
@@ -81,8 +79,7 @@ class DecodeConfig:
 
 CONFIGS = {
     "tiny_causal": PrefillConfig("tiny_causal", 1, 1, 64, 64, 2, 1, 128, True),
-    "cross_attn_rope": PrefillConfig("cross_attn_rope", 2, 4, 64, 128, 8, 8, 32, False,
-                                     rope_base=10000.0),
+    "cross_attn": PrefillConfig("cross_attn", 2, 4, 64, 128, 8, 8, 32, False),
     "qwen3_prefill": PrefillConfig("qwen3_prefill", 3, 4, 2048, 2048, 16, 8, 128, True),
     "paged_decode": DecodeConfig("paged_decode", 4, 256, 16, 8, 128, 16, 256, 128, 4096),
     "long_prefill": PrefillConfig("long_prefill", 5, 1, 32768, 32768, 16, 8, 128, True),
@@ -110,25 +107,6 @@ def normal_f16(shape, seed_words, threads: int = 16) -> np.ndarray:
     return out16.reshape(shape)
 
 
-def rope_interleaved(x16: np.ndarray, base: float) -> np.ndarray:
-    """Rotate pairs (2j, 2j+1) of the last axis by pos * base**(-2j/D).
-
-    ``x16`` is [B, T, H, D] binary16; positions are 0..T-1 along axis 1.
-    Arithmetic in fp64, result rounded to binary16.
-    """
-    B, T, H, D = x16.shape
-    x = x16.astype(np.float64)
-    inv_freq = base ** (-np.arange(0, D, 2, dtype=np.float64) / D)      # [D/2]
-    ang = np.arange(T, dtype=np.float64)[:, None] * inv_freq[None, :]   # [T, D/2]
-    c = np.cos(ang)[None, :, None, :]
-    s = np.sin(ang)[None, :, None, :]
-    xe, xo = x[..., 0::2], x[..., 1::2]
-    out = np.empty_like(x)
-    out[..., 0::2] = xe * c - xo * s
-    out[..., 1::2] = xe * s + xo * c
-    return out.astype(np.float16)
-
-
 def prefill_inputs(cfg: PrefillConfig | str, seed: int = 0):
     """(q, k, v) binary16 arrays for a prefill workload."""
     if isinstance(cfg, str):
@@ -136,10 +114,20 @@ def prefill_inputs(cfg: PrefillConfig | str, seed: int = 0):
     q = normal_f16((cfg.B, cfg.S_q, cfg.H_q, cfg.D), (cfg.config_id, 0, seed))
     k = normal_f16((cfg.B, cfg.S_kv, cfg.H_kv, cfg.D), (cfg.config_id, 1, seed))
     v = normal_f16((cfg.B, cfg.S_kv, cfg.H_kv, cfg.D), (cfg.config_id, 2, seed))
-    if cfg.rope_base is not None:
-        q = rope_interleaved(q, cfg.rope_base)
-        k = rope_interleaved(k, cfg.rope_base)
     return q, k, v
+
+
+def cross_module_inputs(B: int, T_q: int, T_k: int, dim: int, seed: int = 0):
+    """Inputs of the cross-attention module: x_q [B,T_q,dim] and x_kv
+    [B,T_k,dim] standard normal, and four [dim,dim] weights drawn like
+    nn.Linear's default initialisation, uniform in +-1/sqrt(dim), all
+    binary16."""
+    xq = normal_f16((B, T_q, dim), (7, 0, seed))
+    xk = normal_f16((B, T_k, dim), (7, 1, seed))
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([7, 2, seed])))
+    bound = 1.0 / np.sqrt(dim)
+    ws = [g.uniform(-bound, bound, (dim, dim)).astype(np.float16) for _ in range(4)]
+    return xq, xk, ws
 
 
 def paged_layout(seq_lens, block_size: int, max_blocks_per_seq: int, seed_words):
@@ -279,7 +267,7 @@ def ceil_div(a: int, b: int) -> int:
 
 
 __all__ = [
-    "PrefillConfig", "DecodeConfig", "CONFIGS", "normal_f16", "rope_interleaved",
+    "PrefillConfig", "DecodeConfig", "CONFIGS", "normal_f16", "cross_module_inputs",
     "prefill_inputs", "decode_inputs", "paged_layout", "kv_bytes", "PagesLCG",
     "pages_prefill_case", "pages_decode_case", "paginate", "sample_prefill_rows",
     "expected_pairs_decode", "ceil_div",

@@ -12,7 +12,8 @@
  *     nano-vllm" section of the GRPO-CUDA project memory page) with a
  *     log-sum-exp merge.
  * The cache append and the QK-norm + rotary step around them follow the
- * GRPO-CUDA project memory page (sections cited at each declaration).
+ * GRPO-CUDA project memory page, and the cross-attention module the
+ * POPCORNBENCH cross-attention trace (sections cited at each declaration).
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers (HIP device memory or memory the device can
@@ -215,6 +216,45 @@ attn_status_t attn_qk_norm_rope_append(void* q, void* k, const void* v,
                                        float eps, void* k_cache, void* v_cache,
                                        const int64_t* slot_mapping, int block_size,
                                        int64_t num_blocks, void* stream);
+
+/*
+ * Bytes of device workspace attn_cross_attention needs (the projected q, k,
+ * v and the attention output, fp16).  0 for invalid or unsupported
+ * arguments (attn_cross_attention reports those).
+ */
+size_t attn_cross_attention_workspace_size(int B, int T_q, int T_k, int dim, int H);
+
+/*
+ * One layer of multi-head cross-attention with rotary embeddings, the module
+ * of the cross-attention trace (POPCORNBENCH "Kimi-K2.6" page: the problem
+ * statement and its nn.Linear notes): no bias, dropout p = 0.
+ *
+ *   x_q   [B, T_q, dim] fp16        x_kv [B, T_k, dim] fp16
+ *   w_q, w_k, w_v, w_o [dim, dim] fp16, nn.Linear layout [out, in]
+ *   cos_table, sin_table [max_pos, dim/H / 2] fp32 (attn_rope_table with
+ *                         head_dim = dim / H and the module's rotary base)
+ *   out   [B, T_q, dim] fp16 (written)
+ *
+ *   Q = x_q w_q^T,  K = x_kv w_k^T,  V = x_kv w_v^T; head h is columns
+ *   h*D .. h*D+D-1 (D = dim / H).  Q and K rows are rotated over adjacent
+ *   pairs (2j, 2j+1) by the angle of their position in the sequence
+ *   (0..T-1) and pair j; then per head softmax(Q K^T / sqrt(D)) V without a
+ *   mask; out = concat(heads) w_o^T.
+ *
+ * Three launches on `stream`: the Q/K/V projections with the rotation, the
+ * attention (the non-causal prefill kernel), the output projection.  fp32
+ * accumulation; the projected Q, K, V and the attention output are rounded
+ * to fp16 in between (the MFMA operand precision).  workspace: at least
+ * attn_cross_attention_workspace_size(...) bytes, 256-byte aligned (NULL or
+ * smaller is ATTN_ERR_WORKSPACE).  D must be 32, 64 or 128, dim a multiple
+ * of 32, max_pos >= max(T_q, T_k).
+ */
+attn_status_t attn_cross_attention(const void* x_q, const void* x_kv, const void* w_q,
+                                   const void* w_k, const void* w_v, const void* w_o,
+                                   const float* cos_table, const float* sin_table,
+                                   int max_pos, void* out, int B, int T_q, int T_k, int dim,
+                                   int H, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "attn_abi_version", "attn_status_string", "attn_prefill",
         "attn_decode_paged_workspace_size", "attn_decode_paged", "attn_kv_append",
-        "attn_rope_table", "attn_qk_norm_rope", "attn_qk_norm_rope_append"])
+        "attn_rope_table", "attn_qk_norm_rope", "attn_qk_norm_rope_append",
+        "attn_cross_attention_workspace_size", "attn_cross_attention"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -185,3 +186,28 @@ def qk_rope_append(lib, v=P, kc=P2, vc=P2, sm=P, bs=16, nb=4, n=16, D=128):
 ])
 def test_qk_norm_rope_append_rejects(lib, kw, want):
     assert qk_rope_append(lib, **kw) == want
+
+
+def cross(lib, xq=P, xk=P, wq=P, wk=P, wv=P, wo=P, c=P, s=P2, max_pos=128, out=P2, B=4, T_q=64,
+          T_k=128, dim=256, H=8, ws=ctypes.c_void_p(0x40000), wsb=1 << 20):
+    return lib.attn_cross_attention(xq, xk, wq, wk, wv, wo, c, s, max_pos, out, B, T_q, T_k, dim, H, ws,
+                                    wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(xq=NULL), INV), (dict(wo=NULL), INV), (dict(c=NULL), INV), (dict(out=NULL), INV),
+    (dict(B=0), INV), (dict(T_q=0), INV), (dict(T_k=-1), INV), (dict(dim=0), INV), (dict(H=0), INV),
+    (dict(H=3), INV), (dict(H=16), UNS), (dict(H=1), UNS), (dict(dim=48, H=1), UNS), (dict(dim=80, H=1), UNS),
+    (dict(max_pos=127), INV), (dict(xq=ctypes.c_void_p(0x10008)), INV),
+    (dict(ws=NULL), WS), (dict(wsb=1000), WS), (dict(ws=ctypes.c_void_p(0x40010)), WS),
+])
+def test_cross_attention_rejects(lib, kw, want):
+    assert cross(lib, **kw) == want
+
+
+def test_cross_attention_workspace_size(lib):
+    # q and the attention output 4*64*256*2 bytes each, k and v 4*128*256*2 each
+    assert lib.attn_cross_attention_workspace_size(4, 64, 128, 256, 8) == 2 * 131072 + 2 * 262144
+    assert lib.attn_cross_attention_workspace_size(1, 3, 5, 64, 2) == 2 * 512 + 2 * 768
+    assert lib.attn_cross_attention_workspace_size(4, 64, 128, 256, 3) == 0
+    assert lib.attn_cross_attention_workspace_size(4, 64, 128, 256, 16) == 0

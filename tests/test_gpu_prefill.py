@@ -28,7 +28,7 @@ def _rand(shape, seed, scale=1.0):
         (W.normal_f16(shape, (99, seed)).astype(np.float32) * scale).astype(np.float16)
 
 
-@pytest.mark.parametrize("name", ["tiny_causal", "cross_attn_rope"])
+@pytest.mark.parametrize("name", ["tiny_causal", "cross_attn"])
 def test_small_configs_full(name):
     cfg = W.CONFIGS[name]
     q, k, v = W.prefill_inputs(cfg)
