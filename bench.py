@@ -51,6 +51,10 @@ KERNEL_SOURCES = {
                            "attention_attn_prefill_amd/csrc/attn_internal.h"],
     "decode_split_kernel": ["attention_attn_prefill_amd/csrc/decode_paged.hip",
                             "attention_attn_prefill_amd/csrc/attn_internal.h"],
+    "kv_append_kernel": ["attention_attn_prefill_amd/csrc/kv_append.hip",
+                         "attention_attn_prefill_amd/csrc/attn_internal.h"],
+    "qk_norm_rope_kernel": ["attention_attn_prefill_amd/csrc/rope_norm.hip",
+                            "attention_attn_prefill_amd/csrc/attn_internal.h"],
 }
 
 
@@ -124,7 +128,7 @@ def cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl, target_s):
     }
 
 
-def time_kv_append(pcfg, k, v, dev, stream, W, iters=100):
+def time_kv_append(pcfg, k, v, dev, stream, W, traffic_key, iters=100):
     """The prefill's K/V (B*S tokens) written into a paged cache through a
     permuted block table: HBM bytes = read + write of every row."""
     import torch
@@ -153,10 +157,11 @@ def time_kv_append(pcfg, k, v, dev, stream, W, iters=100):
     return {"metric": "paged KV append GB/s (read + write)", "value": round(gbs, 1), "unit": "GB/s",
             "tokens": int(kn.shape[0]), "bytes": int(nbytes), "launch_ms": round(ms, 5),
             "roofline": {"bound": "hbm", "kernel": "kv_append_kernel", "achieved": round(gbs, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(traffic_key, "kv_append_kernel")}}
 
 
-def time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, iters=100):
+def time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key, iters=100):
     """The Qwen3 step between the projections and attention on the prefill's
     B*S tokens: QK RMSNorm + NeoX RoPE in place, fused with the paged append
     of the rotated K and of V (theta 1e6, positions 0..S-1 per sequence).
@@ -206,7 +211,49 @@ def time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, iters=100):
             "tokens": n, "bytes": int(nbytes), "launch_ms": round(ms, 5),
             "roofline": {"bound": "hbm", "kernel": "qk_norm_rope_kernel<128,append>",
                          "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(traffic_key, "qk_norm_rope_kernel")}}
+
+
+def time_cross_module(dev, stream, W, iters=200):
+    """The cross-attention module at the pages' shape (B=4, T_q=64, T_k=128,
+    dim=256, 8 heads of 32, rotary base 1e4): three launches per call.
+    Algorithmic flops: the four projections (2*rows*dim*dim each) and the
+    attention (4*B*H*T_q*T_k*D)."""
+    import torch
+
+    from attention_attn_prefill_amd import (attn_cross_attention, attn_cross_attention_workspace_size,
+                                            attn_rope_table)
+    B, T_q, T_k, dim, H = 4, 64, 128, 256, 8
+    xq, xk, ws = W.cross_module_inputs(B, T_q, T_k, dim, seed=0)
+    txq, txk = torch.from_numpy(xq).to(dev), torch.from_numpy(xk).to(dev)
+    tws = [torch.from_numpy(w).to(dev) for w in ws]
+    ct = torch.empty((T_k, dim // H // 2), dtype=torch.float32, device=dev)
+    st = torch.empty_like(ct)
+    attn_rope_table(ct, st, 1e4, stream=stream)
+    wsb = torch.empty(attn_cross_attention_workspace_size(B, T_q, T_k, dim, H), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T_q, dim), dtype=torch.float16, device=dev)
+
+    def run():
+        attn_cross_attention(txq, txk, *tws, ct, st, out, H, wsb, stream=stream)
+
+    for _ in range(20):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    flops = 2 * B * T_q * dim * dim * 2 + 2 * B * T_k * dim * dim * 2 + 4 * B * H * T_q * T_k * (dim // H)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"metric": "cross-attention module latency", "value": round(ms * 1e3, 2), "unit": "us per call",
+            "higher_is_better": False, "flops": int(flops), "tflops": round(tf, 3), "launches": 3,
+            "config": {"B": B, "T_q": T_q, "T_k": T_k, "dim": dim, "heads": H},
+            "roofline": {"bound": "mfma", "kernel": "proj_kernel + prefill_fwd_kernel<32,noncausal>",
+                         "achieved": round(tf, 3), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP16_TFLOPS, 5)}}
 
 
 def main():
@@ -328,8 +375,9 @@ def main():
             },
         },
     }
-    line["kv_append"] = time_kv_append(pcfg, k, v, dev, stream, W)
-    line["qk_norm_rope_append"] = time_qk_norm_rope(pcfg, q, k, v, dev, stream, W)
+    line["kv_append"] = time_kv_append(pcfg, k, v, dev, stream, W, traffic_key)
+    line["qk_norm_rope_append"] = time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key)
+    line["cross_attention_module"] = time_cross_module(dev, stream, W)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl,
