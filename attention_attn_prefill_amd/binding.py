@@ -62,6 +62,11 @@ def load_library():
     lib.attn_cross_attention_workspace_size.restype = SZ
     lib.attn_cross_attention.argtypes = [P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, P, SZ, P]
     lib.attn_cross_attention.restype = I
+    lib.attn_decode_paged_shared_prefix_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+    lib.attn_decode_paged_shared_prefix_workspace_size.restype = SZ
+    lib.attn_decode_paged_shared_prefix.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I64, P, P, I, I, P,
+                                                    SZ, P]
+    lib.attn_decode_paged_shared_prefix.restype = I
     _lib = lib
     return lib
 
@@ -285,3 +290,43 @@ def attn_cross_attention(x_q, x_kv, w_q, w_k, w_v, w_o, cos_table, sin_table, ou
                                              _stream_handle(stream, x_q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_cross_attention")
+
+
+def attn_decode_paged_shared_prefix_workspace_size(num_seqs: int, H_q: int, H_kv: int, head_dim: int,
+                                                   max_blocks_per_seq: int, block_size: int,
+                                                   num_groups: int, max_group_size: int) -> int:
+    return int(load_library().attn_decode_paged_shared_prefix_workspace_size(
+        num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size, num_groups, max_group_size))
+
+
+def attn_decode_paged_shared_prefix(q, k_cache, v_cache, out, block_tables, seq_lens, group_start,
+                                    prefix_blocks, max_group_size: int, workspace, stream=None) -> None:
+    """Paged decode of forked sequences via ``attn_decode_paged_shared_prefix``:
+    as ``attn_decode_paged``, with int32 ``group_start`` [num_groups + 1]
+    (sequences group_start[i]..group_start[i+1]-1 form group i) and int32
+    ``prefix_blocks`` [num_groups] (leading table entries every sequence of
+    the group shares); workspace: a uint8 device tensor of at least
+    ``attn_decode_paged_shared_prefix_workspace_size`` bytes."""
+    import torch
+    num_seqs, H_q, D = q.shape
+    num_blocks, H_kv, block_size, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, caches, out")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs or \
+            tuple(seq_lens.shape) != (num_seqs,):
+        raise ValueError("block_tables / seq_lens shape mismatch")
+    num_groups = prefix_blocks.numel()
+    if group_start.numel() != num_groups + 1:
+        raise ValueError("group_start must have num_groups + 1 entries")
+    ptrs = [_dev_tensor(x, torch.float16, n) for x, n in
+            ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out"))]
+    ints = [_dev_tensor(x, torch.int32, n) for x, n in
+            ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (group_start, "group_start"),
+             (prefix_blocks, "prefix_blocks"))]
+    ws = _dev_tensor(workspace, torch.uint8, "workspace")
+    st = load_library().attn_decode_paged_shared_prefix(
+        *ptrs, ints[0], ints[1], num_seqs, H_q, H_kv, D, block_tables.shape[1], block_size, num_blocks,
+        ints[2], ints[3], num_groups, int(max_group_size), ws, workspace.numel(),
+        _stream_handle(stream, q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_paged_shared_prefix")

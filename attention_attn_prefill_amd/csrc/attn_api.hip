@@ -151,8 +151,103 @@ ATTN_EXPORT attn_status_t attn_decode_paged(const void* q, const void* k_cache, 
   a.split_blocks = plan.split_blocks;
   a.n_split_max = plan.n_split_max;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  a.group_start = nullptr;  // plain decode
+  a.prefix_blocks = nullptr;
+  a.num_groups = 0;
+  a.max_group_size = 0;
+  a.prefix_slots = 0;
+  a.slot_stride = plan.n_split_max;
   const hipError_t e = attn::launch_decode(a, H_q / H_kv, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+// ---- shared-prefix (forked) paged decode ----------------------------------
+// Workspace: per (sequence, query head) the prefix-chunk partials and the
+// suffix-split partials: slot_stride * (D + 2) floats.
+struct SharedPlan {
+  int split_blocks, n_split_max, prefix_slots;
+  int64_t ws_bytes;
+};
+
+static SharedPlan plan_shared(int num_seqs, int H_q, int H_kv, int max_blocks_per_seq) {
+  SharedPlan p;
+  p.split_blocks = attn::decode_split_blocks(num_seqs, H_kv, max_blocks_per_seq);
+  p.n_split_max = (int)ceil_div64(max_blocks_per_seq, p.split_blocks);
+  p.prefix_slots = (int)ceil_div64(max_blocks_per_seq, attn::kPrefixChunkBlocks);
+  p.ws_bytes = (int64_t)num_seqs * H_q * (p.prefix_slots + p.n_split_max) * (attn::kDecodeHeadDim + 2) * 4;
+  return p;
+}
+
+static attn_status_t check_shared(int num_seqs, int H_q, int H_kv, int head_dim, int max_blocks_per_seq,
+                                  int block_size, int num_groups, int max_group_size) {
+  const attn_status_t st = check_decode_shape(num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size);
+  if (st != ATTN_OK) return st;
+  if (num_groups <= 0 || num_groups > num_seqs || max_group_size <= 0 || max_group_size > num_seqs)
+    return ATTN_ERR_INVALID_ARG;
+  const SharedPlan p = plan_shared(num_seqs, H_q, H_kv, max_blocks_per_seq);
+  const int64_t col_blocks = ceil_div64((int64_t)max_group_size * (H_q / H_kv), 32);
+  if ((int64_t)p.prefix_slots * num_groups * H_kv * col_blocks > (int64_t)0x7fffffff ||
+      (int64_t)p.n_split_max * H_kv * num_seqs > (int64_t)0x7fffffff)
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+ATTN_EXPORT size_t attn_decode_paged_shared_prefix_workspace_size(int num_seqs, int H_q, int H_kv,
+                                                                 int head_dim, int max_blocks_per_seq,
+                                                                 int block_size, int num_groups,
+                                                                 int max_group_size) {
+  if (check_shared(num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size, num_groups,
+                   max_group_size) != ATTN_OK)
+    return 0;
+  return (size_t)plan_shared(num_seqs, H_q, H_kv, max_blocks_per_seq).ws_bytes;
+}
+
+ATTN_EXPORT attn_status_t attn_decode_paged_shared_prefix(
+    const void* q, const void* k_cache, const void* v_cache, void* out, const int32_t* block_tables,
+    const int32_t* seq_lens, int num_seqs, int H_q, int H_kv, int head_dim, int max_blocks_per_seq,
+    int block_size, int64_t num_blocks, const int32_t* group_start, const int32_t* prefix_blocks,
+    int num_groups, int max_group_size, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens || !group_start || !prefix_blocks)
+    return ATTN_ERR_INVALID_ARG;
+  const attn_status_t st = check_shared(num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size,
+                                        num_groups, max_group_size);
+  if (st != ATTN_OK) return st;
+  if (num_blocks <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(group_start, 4) ||
+      !aligned(prefix_blocks, 4))
+    return ATTN_ERR_INVALID_ARG;
+  const SharedPlan plan = plan_shared(num_seqs, H_q, H_kv, max_blocks_per_seq);
+  if (!workspace || (int64_t)workspace_bytes < plan.ws_bytes || !aligned(workspace, 16))
+    return ATTN_ERR_WORKSPACE;
+
+  attn::DecodeArgs a;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_cache = static_cast<const _Float16*>(k_cache);
+  a.v_cache = static_cast<const _Float16*>(v_cache);
+  a.out = static_cast<_Float16*>(out);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  const int64_t slots = (int64_t)num_seqs * H_q * (plan.prefix_slots + plan.n_split_max);
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_o + slots * attn::kDecodeHeadDim;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.split_blocks = plan.split_blocks;
+  a.n_split_max = plan.n_split_max;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  a.group_start = group_start;
+  a.prefix_blocks = prefix_blocks;
+  a.num_groups = num_groups;
+  a.max_group_size = max_group_size;
+  a.prefix_slots = plan.prefix_slots;
+  a.slot_stride = plan.prefix_slots + plan.n_split_max;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (attn::launch_decode_prefix(a, H_q / H_kv, s) != hipSuccess) return ATTN_ERR_LAUNCH;
+  return attn::launch_decode(a, H_q / H_kv, s) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 ATTN_EXPORT attn_status_t attn_kv_append(const void* k_new, const void* v_new, void* k_cache,

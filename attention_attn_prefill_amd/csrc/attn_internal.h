@@ -40,6 +40,17 @@ struct DecodeArgs {
   int split_blocks;  // KV blocks per split
   int n_split_max;   // ceil(max_blocks_per_seq / split_blocks)
   float scale_log2;
+  // Shared-prefix (cascade) mode, off when group_start is null: sequences
+  // group_start[i] .. group_start[i+1]-1 share their first prefix_blocks[i]
+  // table entries.  Those blocks are attended once per group by the prefix
+  // kernel (partials in slots [0, prefix_slots)); the split kernel covers the
+  // rest (slots prefix_slots + split); every row goes through the merge.
+  const int32_t* group_start;
+  const int32_t* prefix_blocks;
+  int num_groups;
+  int max_group_size;
+  int prefix_slots;         // ceil(max_blocks_per_seq / kPrefixChunkBlocks), 0 when off
+  int slot_stride;          // workspace slots per (sequence, query head)
 };
 
 struct KvAppendArgs {
@@ -101,5 +112,28 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_pos, int head_d
 constexpr int kDecodeBlockSize = 16;
 constexpr int kDecodeHeadDim = 128;
 int decode_split_blocks(int num_seqs, int H_kv, int max_blocks_per_seq);
+constexpr int kPrefixChunkBlocks = 32;  // prefix blocks per prefix-kernel workgroup
+
+// Shared-prefix mode: the group gi of sequence s (group_start ascending,
+// group_start[0] = 0, group_start[num_groups] = num_seqs) and its shared
+// leading blocks.  False when the arrays break those rules for s, the prefix
+// is negative or wider than the table, or the group exceeds max_group_size;
+// the merge then reports NaN for the sequence.
+__device__ __forceinline__ bool decode_group_of(const DecodeArgs& a, int s, int& gi, int& skip) {
+  int lo = 0, hi = a.num_groups;
+  if (a.group_start[0] > s || a.group_start[hi] <= s) return false;
+  while (hi - lo > 1) {  // largest lo with group_start[lo] <= s
+    const int mid = (lo + hi) >> 1;
+    if (a.group_start[mid] <= s) lo = mid;
+    else hi = mid;
+  }
+  if (a.group_start[lo + 1] <= s) return false;
+  gi = lo;
+  skip = a.prefix_blocks[lo];
+  return skip >= 0 && skip <= a.max_blocks_per_seq && a.group_start[lo] >= 0 &&
+         a.group_start[lo + 1] <= a.num_seqs &&
+         a.group_start[lo + 1] - a.group_start[lo] <= a.max_group_size;
+}
+hipError_t launch_decode_prefix(const DecodeArgs& a, int group, hipStream_t stream);
 
 }  // namespace attn

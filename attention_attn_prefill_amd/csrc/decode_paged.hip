@@ -92,12 +92,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int cap = a.max_blocks_per_seq * BS;
   const bool len_bad = L_raw > cap;
   const int L = len_bad ? cap : L_raw;
-  const int n_split = L > 0 ? (L + a.split_blocks * BS - 1) / (a.split_blocks * BS) : 0;
-  const bool direct = n_split <= 1;  // this workgroup writes the final output
+  // shared-prefix mode: the first `skip` blocks belong to the group's prefix
+  int skip = 0;
+  if (a.group_start) {
+    int gi;
+    if (!decode_group_of(a, s, gi, skip)) return;  // reported by the merge
+  }
+  const int rem_blocks = (L + BS - 1) / BS - skip;
+  const int n_split = (L > 0 && rem_blocks > 0) ? (rem_blocks + a.split_blocks - 1) / a.split_blocks : 0;
+  // this workgroup writes the final output (plain decode, one split)
+  const bool direct = n_split <= 1 && !a.group_start;
 
   if (L <= 0) {
-    // zero-length context: an all-zero row, written once
-    if (split == 0) {
+    // zero-length context: an all-zero row, written once (by the merge in
+    // shared-prefix mode)
+    if (split == 0 && !a.group_start) {
       for (int idx = tid; idx < G * D; idx += kThreads) {
         const int j = idx / D, d = idx - j * D;
         a.out[((int64_t)s * a.H_q + g * G + j) * D + d] = (_Float16)0.0f;
@@ -110,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   if (tid == 0) sm_bad = len_bad ? 1 : 0;
   __syncthreads();
 
-  const int blk_begin = split * a.split_blocks;
+  const int blk_begin = skip + split * a.split_blocks;
   const int blk_end = min(blk_begin + a.split_blocks, (L + BS - 1) / BS);
 
   half8_t qv[G];
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     if (direct) {
       a.out[((int64_t)s * a.H_q + h) * D + d] = (_Float16)(Os / Ls);
     } else {
-      const int64_t slot = ((int64_t)s * a.H_q + h) * a.n_split_max + split;
+      const int64_t slot = ((int64_t)s * a.H_q + h) * a.slot_stride + a.prefix_slots + split;
       a.ws_o[slot * D + d] = Os;
       if (d == 0) {
         a.ws_ml[slot * 2 + 0] = M;
@@ -259,7 +268,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup of D threads per (sequence, query head): merge the splits.
+// One workgroup of D threads per (sequence, query head): merge the splits
+// (and, in shared-prefix mode, the group's prefix chunks).
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int s = blockIdx.x / a.H_q;
   const int h = blockIdx.x - s * a.H_q;
@@ -267,19 +277,39 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int L_raw = a.seq_lens[s];
   const int cap = a.max_blocks_per_seq * BS;
   const int L = L_raw > cap ? cap : L_raw;
-  const int n_split = L > 0 ? (L + a.split_blocks * BS - 1) / (a.split_blocks * BS) : 0;
-  if (n_split <= 1) return;  // finished by the split kernel
-  const int64_t base = ((int64_t)s * a.H_q + h) * a.n_split_max;
-  float M = -INFINITY;
-  for (int c = 0; c < n_split; ++c) M = fmaxf(M, a.ws_ml[(base + c) * 2]);
-  float Ls = 0.0f, Os = 0.0f;
-  for (int c = 0; c < n_split; ++c) {
-    const float mc = a.ws_ml[(base + c) * 2];
-    const float w = (mc == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mc - M);
-    Ls = fmaf(a.ws_ml[(base + c) * 2 + 1], w, Ls);
-    Os = fmaf(a.ws_o[(base + c) * D + d], w, Os);
+  _Float16* dst = a.out + ((int64_t)s * a.H_q + h) * D + d;
+  const int64_t base = ((int64_t)s * a.H_q + h) * a.slot_stride;
+  int n_pre = 0, first_split = 0, skip = 0;
+  if (a.group_start) {
+    if (L_raw <= 0) {
+      *dst = (_Float16)0.0f;
+      return;
+    }
+    int gi;
+    // the prefix must fit the sequence (whole blocks of visible tokens)
+    if (!decode_group_of(a, s, gi, skip) || L_raw > cap || skip * BS > L) {
+      *dst = (_Float16)__builtin_nanf("");
+      return;
+    }
+    n_pre = (skip + kPrefixChunkBlocks - 1) / kPrefixChunkBlocks;
+    first_split = a.prefix_slots;
   }
-  a.out[((int64_t)s * a.H_q + h) * D + d] = (_Float16)(Os / Ls);
+  const int rem_blocks = (L + BS - 1) / BS - skip;
+  const int n_split = (L > 0 && rem_blocks > 0) ? (rem_blocks + a.split_blocks - 1) / a.split_blocks : 0;
+  if (!a.group_start && n_split <= 1) return;  // finished by the split kernel
+  float M = -INFINITY;
+  for (int c = 0; c < n_pre; ++c) M = fmaxf(M, a.ws_ml[(base + c) * 2]);
+  for (int c = 0; c < n_split; ++c) M = fmaxf(M, a.ws_ml[(base + first_split + c) * 2]);
+  float Ls = 0.0f, Os = 0.0f;
+  auto add = [&](int64_t slot) {
+    const float mc = a.ws_ml[slot * 2];
+    const float w = (mc == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mc - M);
+    Ls = fmaf(a.ws_ml[slot * 2 + 1], w, Ls);
+    Os = fmaf(a.ws_o[slot * D + d], w, Os);
+  };
+  for (int c = 0; c < n_pre; ++c) add(base + c);
+  for (int c = 0; c < n_split; ++c) add(base + first_split + c);
+  *dst = (_Float16)(Os / Ls);
 }
 
 template <int G>
@@ -288,7 +318,7 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   void* kargs[] = {&args};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<G>),
                                  dim3((unsigned)((int64_t)a.n_split_max * a.H_kv * a.num_seqs)), dim3(kThreads), kargs, 0, stream);
-  if (e != hipSuccess || a.n_split_max <= 1) return e;
+  if (e != hipSuccess || (a.n_split_max <= 1 && !a.group_start)) return e;
   return hipLaunchKernel(reinterpret_cast<const void*>(&decode_merge_kernel),
                          dim3((unsigned)(a.num_seqs * a.H_q)), dim3(D), kargs, 0, stream);
 }

@@ -130,6 +130,85 @@ def cross_module_inputs(B: int, T_q: int, T_k: int, dim: int, seed: int = 0):
     return xq, xk, ws
 
 
+def forked_decode_inputs(group_sizes, prompt_lens, suffix_lens, H_q: int, H_kv: int, D: int = 128,
+                         block_size: int = 16, seed: int = 0):
+    """Paged decode inputs of forked sequences (a GRPO group samples several
+    completions of one prompt).  Group i has ``group_sizes[i]`` sequences
+    that share a prompt of ``prompt_lens[i]`` tokens; sequence j of the
+    flattened order then has ``suffix_lens[j]`` tokens of its own.
+
+    The prompt's whole blocks are one physical copy that every table of the
+    group points to (a fork copies table entries, not K/V); a partial last
+    prompt block is copied into each sequence's own blocks (same prompt
+    K/V).  Physical block ids are a seeded permutation.  Returns
+    (q, k_cache, v_cache, block_tables, seq_lens, group_start, prefix_blocks).
+    """
+    group_sizes = [int(x) for x in group_sizes]
+    n = sum(group_sizes)
+    suffix_lens = [int(x) for x in suffix_lens]
+    assert len(suffix_lens) == n and len(prompt_lens) == len(group_sizes)
+    bs = block_size
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([8, seed])))
+    seq_lens = []
+    blocks_needed = 0
+    for gi, G in enumerate(group_sizes):
+        P = int(prompt_lens[gi])
+        blocks_needed += P // bs
+        for j in range(G):
+            L = P + suffix_lens[len(seq_lens)]
+            seq_lens.append(L)
+            blocks_needed += (L + bs - 1) // bs - P // bs
+    max_bps = max((L + bs - 1) // bs for L in seq_lens)
+    perm = rng.permutation(blocks_needed).astype(np.int32)
+    k_cache = normal_f16((blocks_needed, H_kv, bs, D), (8, 1, seed))
+    v_cache = normal_f16((blocks_needed, H_kv, bs, D), (8, 2, seed))
+    bt = np.full((n, max_bps), -1, np.int32)
+    group_start = [0]
+    prefix_blocks = []
+    nxt = 0
+    s = 0
+    for gi, G in enumerate(group_sizes):
+        P = int(prompt_lens[gi])
+        shared = perm[nxt:nxt + P // bs]
+        nxt += P // bs
+        prefix_blocks.append(P // bs)
+        # K/V of the partial prompt block, copied into every sequence's own block
+        part_src = None
+        for j in range(G):
+            L = seq_lens[s]
+            own = (L + bs - 1) // bs - P // bs
+            ids = perm[nxt:nxt + own]
+            nxt += own
+            bt[s, :P // bs] = shared
+            bt[s, P // bs:P // bs + own] = ids
+            if P % bs and own > 0:
+                if part_src is None:
+                    part_src = int(ids[0])
+                else:
+                    k_cache[ids[0], :, :P % bs] = k_cache[part_src, :, :P % bs]
+                    v_cache[ids[0], :, :P % bs] = v_cache[part_src, :, :P % bs]
+            s += 1
+        group_start.append(s)
+    q = normal_f16((n, H_q, D), (8, 3, seed))
+    return (q, k_cache, v_cache, bt, np.array(seq_lens, np.int32), np.array(group_start, np.int32),
+            np.array(prefix_blocks, np.int32))
+
+
+GRPO_DECODE = dict(num_groups=32, group_size=8, prompt=2048, suffix_lo=1, suffix_hi=512, H_q=16, H_kv=8)
+
+
+def grpo_decode_inputs(seed: int = 0):
+    """The forked-decode workload: 32 prompts of 2048 tokens, 8 samples each
+    with U[1, 512] generated tokens of their own (256 sequences, H_q 16,
+    H_kv 8, D 128, 16-token blocks)."""
+    c = GRPO_DECODE
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([9, seed])))
+    n = c["num_groups"] * c["group_size"]
+    suffix = rng.integers(c["suffix_lo"], c["suffix_hi"], n, endpoint=True)
+    return forked_decode_inputs([c["group_size"]] * c["num_groups"], [c["prompt"]] * c["num_groups"], suffix,
+                                c["H_q"], c["H_kv"], seed=seed)
+
+
 def paged_layout(seq_lens, block_size: int, max_blocks_per_seq: int, seed_words):
     """Block tables for ``seq_lens``: a seeded permutation of the physical
     blocks, assigned in (sequence, logical block) order; unused entries -1."""
@@ -267,7 +346,7 @@ def ceil_div(a: int, b: int) -> int:
 
 
 __all__ = [
-    "PrefillConfig", "DecodeConfig", "CONFIGS", "normal_f16", "cross_module_inputs",
+    "PrefillConfig", "DecodeConfig", "CONFIGS", "normal_f16", "cross_module_inputs", "forked_decode_inputs", "grpo_decode_inputs", "GRPO_DECODE",
     "prefill_inputs", "decode_inputs", "paged_layout", "kv_bytes", "PagesLCG",
     "pages_prefill_case", "pages_decode_case", "paginate", "sample_prefill_rows",
     "expected_pairs_decode", "ceil_div",

@@ -130,6 +130,61 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache,
                                 void* stream);
 
 /*
+ * Bytes of device workspace attn_decode_paged_shared_prefix needs; 0 for
+ * invalid or unsupported arguments.
+ */
+size_t attn_decode_paged_shared_prefix_workspace_size(int num_seqs, int H_q, int H_kv,
+                                                      int head_dim, int max_blocks_per_seq,
+                                                      int block_size, int num_groups,
+                                                      int max_group_size);
+
+/*
+ * Paged decode of forked sequences: the result of attn_decode_paged over the
+ * same arguments, with every group's shared prompt blocks read once for the
+ * whole group instead of once per sequence (cascade attention).  GRPO
+ * samples several completions of one prompt, and the engine forks the
+ * prompt's cache by copying table entries only ("GRPO-CUDA Project Memory"
+ * page, "KV Cache design": paged_kv_cache_fork, no KV copy).
+ *
+ *   q, k_cache, v_cache, out, block_tables, seq_lens, num_seqs, H_q, H_kv,
+ *   head_dim, max_blocks_per_seq, block_size, num_blocks: as attn_decode_paged
+ *   group_start   [num_groups + 1] int32: sequences group_start[i] ..
+ *                 group_start[i+1]-1 form group i (group_start[0] = 0,
+ *                 group_start[num_groups] = num_seqs, nondecreasing)
+ *   prefix_blocks [num_groups] int32: the number of leading table entries
+ *                 that every sequence of group i shares (the prompt's whole
+ *                 blocks; 0 = no sharing)
+ *   max_group_size: an upper bound on every group's size
+ *
+ * Each group's prefix is attended once per kv head for all of its query
+ * rows (group size x H_q/H_kv of them, in MFMA column blocks of 32), through
+ * the table of the group's first sequence; every sequence's remaining blocks
+ * go through the split-K decode kernel; a merge kernel combines the partial
+ * results by log-sum-exp.  Three launches on `stream`.
+ *
+ * workspace: at least attn_decode_paged_shared_prefix_workspace_size(...)
+ * bytes (NULL or smaller is ATTN_ERR_WORKSPACE).
+ * Device-side preconditions, besides those of attn_decode_paged: the group
+ * arrays follow the rules above, every sequence of a group holds at least
+ * prefix_blocks * block_size tokens, and the prefix entries of all tables of
+ * a group are equal (not checked: the first table's entries are used).  A
+ * sequence that breaks a checked one gets NaN rows; seq_lens <= 0 gives an
+ * all-zero row.
+ */
+attn_status_t attn_decode_paged_shared_prefix(const void* q, const void* k_cache,
+                                              const void* v_cache, void* out,
+                                              const int32_t* block_tables,
+                                              const int32_t* seq_lens, int num_seqs,
+                                              int H_q, int H_kv, int head_dim,
+                                              int max_blocks_per_seq, int block_size,
+                                              int64_t num_blocks,
+                                              const int32_t* group_start,
+                                              const int32_t* prefix_blocks,
+                                              int num_groups, int max_group_size,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream);
+
+/*
  * Paged KV append: write new keys and values into the paged caches that
  * attn_decode_paged reads -- the write side of the same data structure
  * ("GRPO-CUDA Project Memory" page, "KV Cache design": slot_mapping[token] =

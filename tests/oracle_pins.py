@@ -35,6 +35,8 @@ What pins what:
                                 numpy RMSNorm then rotation (the pages' order)
   * cross-attention module   -- torch fp64 (F.linear, complex RoPE, SDPA);
                                 identical memory rows; a single key
+  * forked (shared-prefix) decode -- tables sharing the prompt's blocks
+                                give the same result as private copies
 """
 from __future__ import annotations
 
@@ -597,6 +599,29 @@ def pin_cross_attention_single_key(ora):
     got = ora.cross_attention(xq, xk, *ws, H=H)
     want = (_f64(xk[:, 0]) @ _f64(ws[2]).T) @ _f64(ws[3]).T
     assert np.allclose(got, np.broadcast_to(want[:, None, :], got.shape), rtol=1e-12, atol=1e-14)
+
+
+def pin_decode_forked_tables_equal_private_copies(ora):
+    """A fork copies table entries only: decoding sequences whose tables share
+    the prompt's physical blocks equals decoding with a private copy of those
+    blocks per sequence, bit for bit."""
+    q, kc, vc, bt, sl, gs, pb = W.forked_decode_inputs([4, 1, 3], [48, 16, 37], [3, 0, 20, 9, 1, 30, 16, 2],
+                                                       4, 2, D=32, seed=401)
+    shared = ora.decode_paged(q, kc, vc, bt, sl)
+    # give every sequence private copies of its group's shared blocks
+    extra_k, extra_v, bt2 = [kc], [vc], bt.copy()
+    nxt = kc.shape[0]
+    for gi in range(len(pb)):
+        for s in range(gs[gi], gs[gi + 1]):
+            for b in range(pb[gi]):
+                phys = bt[s, b]
+                extra_k.append(kc[phys:phys + 1])
+                extra_v.append(vc[phys:phys + 1])
+                bt2[s, b] = nxt
+                nxt += 1
+    kc2, vc2 = np.concatenate(extra_k), np.concatenate(extra_v)
+    private = ora.decode_paged(q, kc2, vc2, bt2, sl)
+    assert np.array_equal(shared, private)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
         "attn_abi_version", "attn_status_string", "attn_prefill",
         "attn_decode_paged_workspace_size", "attn_decode_paged", "attn_kv_append",
         "attn_rope_table", "attn_qk_norm_rope", "attn_qk_norm_rope_append",
-        "attn_cross_attention_workspace_size", "attn_cross_attention"])
+        "attn_cross_attention_workspace_size", "attn_cross_attention",
+        "attn_decode_paged_shared_prefix_workspace_size", "attn_decode_paged_shared_prefix"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -211,3 +212,34 @@ def test_cross_attention_workspace_size(lib):
     assert lib.attn_cross_attention_workspace_size(1, 3, 5, 64, 2) == 2 * 512 + 2 * 768
     assert lib.attn_cross_attention_workspace_size(4, 64, 128, 256, 3) == 0
     assert lib.attn_cross_attention_workspace_size(4, 64, 128, 256, 16) == 0
+
+
+def shared(lib, q=P, kc=P, vc=P, out=P2, bt=P, sl=P, num_seqs=256, H_q=16, H_kv=8, D=128, mbs=160, bs=16,
+           nb=9000, gs=P, pb=P, ng=32, mgs=8, ws=ctypes.c_void_p(0x40000), wsb=1 << 30):
+    return lib.attn_decode_paged_shared_prefix(q, kc, vc, out, bt, sl, num_seqs, H_q, H_kv, D, mbs, bs, nb, gs,
+                                               pb, ng, mgs, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), INV), (dict(gs=NULL), INV), (dict(pb=NULL), INV), (dict(ng=0), INV),
+    (dict(ng=257), INV), (dict(mgs=0), INV), (dict(mgs=257), INV), (dict(nb=0), INV),
+    (dict(H_q=12), INV), (dict(D=64), UNS), (dict(bs=32), UNS), (dict(H_q=80, H_kv=8), UNS),
+    (dict(gs=ctypes.c_void_p(0x10002)), INV),
+    (dict(ws=NULL), WS), (dict(wsb=1000), WS),
+])
+def test_shared_prefix_rejects(lib, kw, want):
+    assert shared(lib, **kw) == want
+
+
+def test_shared_prefix_workspace_size(lib):
+    # 256 seqs x 16 heads x (prefix slots ceil(160/32)=5 + splits ceil(160/16)=10) x 130 floats
+    split = 16  # 256*8 pairs * ceil(160/split) >= 2048 already at the largest split <= 160 that divides...
+    n = lib.attn_decode_paged_shared_prefix_workspace_size(256, 16, 8, 128, 160, 16, 32, 8)
+    slots_prefix = 5
+    for s_ in (128, 64, 32, 16):
+        if 256 * 8 * ((160 + s_ - 1) // s_) >= 2048:
+            split = s_
+            break
+    assert n == 256 * 16 * (slots_prefix + (160 + split - 1) // split) * 130 * 4
+    assert lib.attn_decode_paged_shared_prefix_workspace_size(256, 16, 8, 128, 160, 16, 0, 8) == 0
+    assert lib.attn_decode_paged_shared_prefix_workspace_size(256, 16, 8, 64, 160, 16, 32, 8) == 0
