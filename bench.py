@@ -256,6 +256,63 @@ def time_cross_module(dev, stream, W, iters=200):
                          "frac": round(tf / PEAK_FP16_TFLOPS, 5)}}
 
 
+def time_shared_prefix(dev, stream, W, iters=50):
+    """The forked-decode workload (32 prompts of 2048 tokens, 8 samples each
+    with U[1, 512] tokens of their own; H 16/8, D 128): plain paged decode
+    against the shared-prefix path on the same tables.  Logical KV bytes count
+    every sequence's context; unique bytes count each shared prompt once."""
+    import torch
+
+    from attention_attn_prefill_amd import (attn_decode_paged, attn_decode_paged_shared_prefix,
+                                            attn_decode_paged_shared_prefix_workspace_size,
+                                            attn_decode_paged_workspace_size)
+    q, kc, vc, bt, sl, gs, pb = W.grpo_decode_inputs()
+    c = W.GRPO_DECODE
+    t = {n: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+         for n, x in (("q", q), ("kc", kc), ("vc", vc), ("bt", bt), ("sl", sl), ("gs", gs), ("pb", pb))}
+    out = torch.empty_like(t["q"])
+    n, Hq, Hkv, D = q.shape[0], q.shape[1], kc.shape[1], q.shape[2]
+    ws_plain = torch.empty(max(16, attn_decode_paged_workspace_size(n, Hq, Hkv, D, bt.shape[1], 16)),
+                           dtype=torch.uint8, device=dev)
+    mgs = c["group_size"]
+    ws_shared = torch.empty(attn_decode_paged_shared_prefix_workspace_size(n, Hq, Hkv, D, bt.shape[1], 16,
+                                                                          len(pb), mgs),
+                            dtype=torch.uint8, device=dev)
+
+    def plain():
+        attn_decode_paged(t["q"], t["kc"], t["vc"], out, t["bt"], t["sl"], workspace=ws_plain, stream=stream)
+
+    def shared():
+        attn_decode_paged_shared_prefix(t["q"], t["kc"], t["vc"], out, t["bt"], t["sl"], t["gs"], t["pb"], mgs,
+                                        ws_shared, stream=stream)
+
+    def timed(fn):
+        for _ in range(10):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    ms_plain, ms_shared = timed(plain), timed(shared)
+    row = Hkv * D * 2 * 2  # K + V bytes per token
+    logical = int(sl.astype(np.int64).sum()) * row
+    shared_tokens = int(np.sum(pb.astype(np.int64) * 16 * (np.diff(gs) - 1)))
+    unique = logical - shared_tokens * row
+    return {"metric": "forked paged decode: logical KV GB/s", "value": round(logical / (ms_shared * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "launch_ms": round(ms_shared, 5), "plain_decode_ms": round(ms_plain, 5),
+            "speedup_vs_plain_decode": round(ms_plain / ms_shared, 3),
+            "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+            "config": dict(c),
+            "roofline": {"bound": "hbm", "kernel": "prefix_chunk_kernel + decode_split_kernel + decode_merge_kernel",
+                         "achieved": round(unique / (ms_shared * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s (unique bytes)",
+                         "frac": round(unique / (ms_shared * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -378,6 +435,7 @@ def main():
     line["kv_append"] = time_kv_append(pcfg, k, v, dev, stream, W, traffic_key)
     line["qk_norm_rope_append"] = time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key)
     line["cross_attention_module"] = time_cross_module(dev, stream, W)
+    line["shared_prefix_decode"] = time_shared_prefix(dev, stream, W)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl,
