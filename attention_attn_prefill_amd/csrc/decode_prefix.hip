@@ -13,19 +13,24 @@
 //     blocks, each re-reading the prefix);
 //   * a workgroup takes kPrefixChunkBlocks prefix blocks (read through the
 //     group's first table row: the prefix entries of every table in the group
-//     are the same blocks); its 4 wavefronts take 32-key tiles (two blocks)
-//     in turn;
-//   * per tile: S^T[32 keys x 32 rows] = K Q^T with v_mfma_f32_32x32x16_f16,
-//     the K operand read straight from the cache (lane l: key l % 32, 16
-//     bytes at dims 8 * (l / 32) + 16 * step), the Q fragment held in VGPRs;
-//     online softmax in the log2 domain (each row's 32 scores sit in lanes l
-//     and l + 32); O^T[D x 32] += V^T P^T with the V tile staged row-major
-//     in the wavefront's own LDS region and the V^T operand read with the
-//     transposing ds_read_b64_tr_b16, P^T taken from the score accumulator;
-//   * the wavefronts merge through LDS and the workgroup writes one partial
-//     (unnormalised o, max, sum) per query row into the decode workspace
-//     slot of its chunk; the decode merge kernel combines these with the
-//     per-sequence suffix splits.
+//     are the same blocks) as 32-key tiles (two blocks);
+//   * the tiles stream through a ring of kStages LDS stages filled by
+//     buffer-to-LDS loads (no registers held while in flight), kStages - 1
+//     tiles ahead; each wavefront fills a quarter of every tile;
+//   * every wavefront computes the whole score tile S^T[32 keys x 32 rows] =
+//     K Q^T with v_mfma_f32_32x32x16_f16 (K from LDS, Q in VGPRs) and the
+//     same online softmax in the log2 domain, and owns one 32-wide slice of
+//     the head dimension of O^T += V^T P^T (V^T read with the transposing
+//     ds_read_b64_tr_b16, P^T taken from the score accumulator), so the
+//     wavefronts never merge: each writes its slice of the partial
+//     (unnormalised o) and wavefront 0 the (max, sum) of every row into the
+//     decode workspace slot of its chunk; the decode merge kernel combines
+//     these with the per-sequence suffix splits.
+// LDS tiles are unpadded 256-byte key rows.  K: 16-byte chunk c of row r sits
+// at chunk c ^ (r % 16), so the 16 rows one K-operand read touches spread
+// over all banks.  V: 64-byte segment s of row r sits at s ^ (r % 4), so the
+// four rows of a transposing read hit four different segments.  The loads
+// put each lane's 16 bytes at the swizzled place directly.
 #include "attn_internal.h"
 
 #include <math.h>
@@ -36,23 +41,37 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int D = kDecodeHeadDim;     // 128
 constexpr int BS = kDecodeBlockSize;  // 16
-constexpr int VROW = D + 32;          // LDS row stride of the V tile (halfs): 4 rows of a tr read hit disjoint banks
 constexpr int CB = kPrefixChunkBlocks;
+constexpr int kStages = 4;
+constexpr int kTileHalfs = 32 * D;    // one 32-key tile of K or V
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ short4_t lds_read_tr(const _Float16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+// The V^T operands of a whole 32-key tile: four transposing reads at the
+// lane's LDS byte address + 0, 8, 16 and 24 rows.  Written as one asm block
+// that waits for its own reads: the compiler cannot tell these reads from
+// the buffer-to-LDS loads still in flight into other stages and would
+// otherwise wait for all of them first; the ring protocol (vmcnt wait and
+// barrier before a tile is read) already orders them.  The outputs are
+// early-clobber: a read's destination must not be the address register
+// that a later read of the block still uses (its data can land before the
+// later read issues).
+__device__ __forceinline__ void lds_read_tr_tile(uint32_t addr, short4_t (&r)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %3, %4 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(addr)
+      : "memory");
 }
 
-// V^T operand of 16 keys (chunk c of the 32-key tile) for d tile dt, in the
-// key order of the P^T operand taken from the score accumulator: keys
-// 16c + 4*hf + (0..3), then 16c + 8 + 4*hf + (0..3).
-__device__ __forceinline__ half8_t pv_operand(const _Float16* vl, int dt, int c) {
-  const short4_t lo = lds_read_tr(vl + 16 * c * VROW + dt * 32);
-  const short4_t hi = lds_read_tr(vl + (16 * c + 8) * VROW + dt * 32);
-  const short4_t lohi[2] = {lo, hi};
-  return __builtin_bit_cast(half8_t, lohi);
+__device__ __forceinline__ uint32_t lds_addr(const _Float16* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) _Float16*)p);
 }
 
 __device__ __forceinline__ float half_swap_max(float x) {
@@ -60,8 +79,31 @@ __device__ __forceinline__ float half_swap_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+__device__ __forceinline__ float half_swap_add(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// buffer resource over one (block, kv head) slab of 4 KB
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const _Float16* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, BS * D * 2, 0x00020000);
+}
+
+template <int kOutstanding>
+__device__ __forceinline__ void wait_tiles() {
+  // each tile costs every lane 4 buffer-to-LDS loads
+  if constexpr (kOutstanding == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (kOutstanding == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if constexpr (kOutstanding == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
 template <int G>
 __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a, int col_blocks) {
+  static_assert(kStages == 4, "wait_tiles covers up to two tiles in flight behind the current one");
   // block id -> (chunk, group, kv head, column block), chunk slowest
   const int per_chunk = a.num_groups * a.H_kv * col_blocks;
   const int chunk = blockIdx.x / per_chunk;
@@ -70,17 +112,14 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a,
   rest /= col_blocks;
   const int g = rest % a.H_kv;
   const int gi = rest / a.H_kv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
 
-  __shared__ __attribute__((aligned(16))) _Float16 v_lds[kWaves][32 * VROW];
-  __shared__ float sm_m[kWaves][32];
-  __shared__ float sm_l[kWaves][32];
-  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][32][D + 4];
-  __shared__ int sm_bad;
+  __shared__ __attribute__((aligned(1024))) _Float16 ring[kStages][2][kTileHalfs];
 
-  // group and chunk extents; anything inconsistent is left to the merge
-  // kernel, which reports NaN for the group's sequences
+  // group and chunk extents (uniform over the workgroup); anything
+  // inconsistent is left to the merge kernel, which reports NaN
   const int gs = a.group_start[gi], ge = a.group_start[gi + 1];
   if (gs < 0 || ge > a.num_seqs || ge < gs || ge - gs > a.max_group_size) return;
   const int rows = (ge - gs) * G;
@@ -89,9 +128,16 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a,
   if (P < 0 || P > a.max_blocks_per_seq) return;
   const int b_begin = chunk * CB;
   if (b_begin >= P) return;
-  const int b_end = min(b_begin + CB, P);
-  if (tid == 0) sm_bad = 0;
-  __syncthreads();
+  const int nb = min(CB, P - b_begin);
+  const int n_tiles = (nb + 1) / 2;
+
+  // the chunk's table entries, one per lane; a bad entry turns the group's
+  // rows NaN and block 0 is read in its place
+  const int32_t* bt = a.block_tables + (int64_t)gs * a.max_blocks_per_seq + b_begin;
+  int ent = lane < nb ? bt[lane] : 0;
+  const bool ent_bad = ent < 0 || (int64_t)ent >= a.num_blocks;
+  const bool bad = __builtin_amdgcn_ballot_w64(ent_bad) != 0;
+  if (ent_bad) ent = 0;
 
   // this lane's query row (MFMA column) and its Q fragment
   const int r = 32 * cb + col;
@@ -103,46 +149,81 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a,
   for (int ks = 0; ks < D / 16; ++ks)
     qf[ks] = valid_row ? *reinterpret_cast<const half8_t*>(a.q + ((int64_t)s * a.H_q + h) * D + 16 * ks + 8 * hf)
                        : half8_t{};
+  // take the Q loads' wait here, before the tile loads are in flight
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
 
-  const int32_t* bt = a.block_tables + (int64_t)gs * a.max_blocks_per_seq;
-  const int64_t slab = (int64_t)a.H_kv * BS * D;  // elements per physical block
+  // loads: wavefront w fills key rows 8w .. 8w + 7 of each tile (block w / 2
+  // of the pair), two 4-row loads of 1 KB for K and two for V; lane i of a
+  // load lands at row R0 + i / 16, 16-byte place i % 16
+  const int64_t slab = (int64_t)a.H_kv * BS * D;
   const int64_t head_off = (int64_t)g * BS * D;
-  _Float16* vl = v_lds[wave];
-  // transposing-read offset of this lane inside the V tile
-  const int v_lane = (4 * hf + (lane & 15) / 4) * VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int voff_k[2], voff_v[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rr = 8 * (wave & 1) + 4 * j + (lane >> 4);  // row inside the block
+    const int pl = lane & 15;                             // place inside the LDS row
+    voff_k[j] = rr * 256 + 16 * (pl ^ rr);
+    voff_v[j] = rr * 256 + 16 * (4 * ((pl >> 2) ^ (rr & 3)) + (pl & 3));
+  }
+  auto issue = [&](int t) {
+    const int e0 = __builtin_amdgcn_readlane(ent, 2 * t);
+    const int e1 = 2 * t + 1 < nb ? __builtin_amdgcn_readlane(ent, 2 * t + 1) : e0;
+    const int64_t blk = (wave < 2 ? e0 : e1) * slab + head_off;
+    const __amdgpu_buffer_rsrc_t kr = slab_rsrc(a.k_cache + blk);
+    const __amdgpu_buffer_rsrc_t vr = slab_rsrc(a.v_cache + blk);
+    _Float16* kd = ring[t % kStages][0] + 8 * wave * D;
+    _Float16* vd = ring[t % kStages][1] + 8 * wave * D;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(kd + 4 * j * D), 16, voff_k[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(vd + 4 * j * D), 16, voff_v[j], 0, 0, 0);
+    }
+  };
+
+  // K operand: key col, 16-byte chunk 2 ks + hf at chunk (2 ks + hf) ^ (col % 16)
+  const int k_row = col * D;
+  const int k_x = col & 15;
+  // V^T operand of 16 keys (chunk c of the tile) for this wavefront's d
+  // slice, in the key order of the P^T operand taken from the score
+  // accumulator (keys 16c + 4hf + 0..3, then 16c + 8 + 4hf + 0..3); the
+  // four rows of a read differ in row % 4 = (lane % 16) / 4
+  const int vq = (lane & 15) >> 2;
+  const int v_lane = (4 * hf + vq) * D + 32 * (wave ^ vq) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   float m = -INFINITY, l = 0.0f;
-  f32x16_t o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
+  f32x16_t o = f32x16_t{};
 
-  const int n_tiles = (b_end - b_begin + 1) / 2;
-  for (int t = wave; t < n_tiles; t += kWaves) {
-    const int b0 = b_begin + 2 * t;
-    const bool has1 = b0 + 1 < b_end;
-    int p0 = bt[b0];
-    int p1 = has1 ? bt[b0 + 1] : p0;
-    if (p0 < 0 || (int64_t)p0 >= a.num_blocks || p1 < 0 || (int64_t)p1 >= a.num_blocks) {
-      sm_bad = 1;  // the group reports NaN; read block 0 instead
-      p0 = p1 = 0;
-    }
-    // K operand: key col (block col / 16, row col % 16)
-    const _Float16* kp = a.k_cache + (int64_t)(col < 16 ? p0 : p1) * slab + head_off + (col & 15) * D + 8 * hf;
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < n_tiles) issue(t);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int ahead = n_tiles - 1 - t;
+    if (ahead >= 2) wait_tiles<2>();
+    else if (ahead == 1) wait_tiles<1>();
+    else wait_tiles<0>();
+    // tile t is in LDS for every wavefront, and every wavefront is done
+    // with tile t - 1, whose stage is refilled next.  A bare barrier: the
+    // waits it needs are explicit (the loads' vmcnt above; every LDS read of
+    // tile t - 1 has been waited for by its consumer), and a fenced barrier
+    // would wait for the tiles still in flight.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + kStages - 1 < n_tiles) issue(t + kStages - 1);
+
+    const _Float16* kl = ring[t % kStages][0];
+    const _Float16* vl = ring[t % kStages][1];
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const half8_t kf = *reinterpret_cast<const half8_t*>(kp + 16 * ks);
+      const half8_t kf = *reinterpret_cast<const half8_t*>(kl + k_row + 8 * ((2 * ks + hf) ^ k_x));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sc, 0, 0, 0);
-    }
-    // stage V rows (key kk = lane / 16 + 4u, dims 8 * (lane % 16)) into LDS
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int kk = (lane >> 4) + 4 * u;
-      const _Float16* vp = a.v_cache + (int64_t)(kk < 16 ? p0 : p1) * slab + head_off + (kk & 15) * D + 8 * (lane & 15);
-      *reinterpret_cast<half8_t*>(vl + kk * VROW + 8 * (lane & 15)) = *reinterpret_cast<const half8_t*>(vp);
     }
     // scores (log2 domain); keys of a missing second block are masked.
     // Accumulator element i holds key 8 * (i / 4) + 4 * hf + i % 4.
+    const bool has1 = 2 * t + 1 < nb;
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -163,56 +244,32 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a,
     }
     l = l * alpha + ps;
     m = m_new;
+    o *= alpha;
+    short4_t vt[4];  // rows +0, +8 (keys 0..15) and +16, +24 (keys 16..31)
+    lds_read_tr_tile(lds_addr(vl + v_lane), vt);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pv_operand(vl + v_lane, dt, c), pf[c], o[dt], 0, 0, 0);
+    for (int c = 0; c < 2; ++c) {
+      const short4_t lohi[2] = {vt[2 * c], vt[2 * c + 1]};
+      o = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, lohi), pf[c], o, 0, 0, 0);
+    }
   }
 
-  // per-wavefront results: row col's sum is split over lanes col, col + 32
-  {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-    const float lrow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (hf == 0) {
-      sm_m[wave][col] = m;
-      sm_l[wave][col] = lrow;
-    }
-    // O^T element (d = dt*32 + 8*(i/4) + 4*hf + i%4, row col)
+  // row col's sum is split over lanes col and col + 32
+  const float lrow = half_swap_add(l);
+  if (!valid_row) return;
+  const float nan = __builtin_nanf("");
+  const int64_t slot = ((int64_t)s * a.H_q + h) * a.slot_stride + chunk;
+  // O^T element i: d = 32 wave + 8 (i / 4) + 4 hf + i % 4, row col
+  float* od = a.ws_o + slot * D + 32 * wave + 4 * hf;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm_o[wave][col][dt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3)] = o[dt][i];
+  for (int q4 = 0; q4 < 4; ++q4) {
+    float4 v4 = {o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]};
+    if (bad) v4 = {nan, nan, nan, nan};
+    *reinterpret_cast<float4*>(od + 8 * q4) = v4;
   }
-  __syncthreads();
-
-  // merge the wavefronts and write one partial per valid row
-  const bool bad = sm_bad != 0;
-  for (int idx = tid; idx < 32 * D; idx += 64 * kWaves) {
-    const int rr = idx / D, d = idx - rr * D;
-    const int row = 32 * cb + rr;
-    if (row >= rows) continue;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][rr]);
-    float Ls = 0.0f, Os = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_m[w][rr];
-      const float wt = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-      Ls = fmaf(sm_l[w][rr], wt, Ls);
-      Os = fmaf(sm_o[w][rr][d], wt, Os);
-    }
-    if (bad) M = Ls = Os = __builtin_nanf("");
-    const int ss = gs + row / G, hh = g * G + row % G;
-    const int64_t slot = ((int64_t)ss * a.H_q + hh) * a.slot_stride + chunk;
-    a.ws_o[slot * D + d] = Os;
-    if (d == 0) {
-      a.ws_ml[slot * 2 + 0] = M;
-      a.ws_ml[slot * 2 + 1] = Ls;
-    }
+  if (wave == 0 && hf == 0) {
+    a.ws_ml[slot * 2 + 0] = bad ? nan : m;
+    a.ws_ml[slot * 2 + 1] = bad ? nan : lrow;
   }
 }
 
