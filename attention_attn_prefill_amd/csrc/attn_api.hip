@@ -172,6 +172,11 @@ struct SharedPlan {
 static SharedPlan plan_shared(int num_seqs, int H_q, int H_kv, int max_blocks_per_seq) {
   SharedPlan p;
   p.split_blocks = attn::decode_split_blocks(num_seqs, H_kv, max_blocks_per_seq);
+  // Enough (sequence, kv head) pairs to fill the chip with one workgroup
+  // each: one split per sequence, so the split kernel folds in the prefix
+  // partials and no merge kernel runs.  The private part of a forked
+  // sequence is its generated tokens, short next to the shared prompt.
+  if ((int64_t)num_seqs * H_kv >= attn::kDecodeSingleSplitPairs) p.split_blocks = max_blocks_per_seq;
   p.n_split_max = (int)ceil_div64(max_blocks_per_seq, p.split_blocks);
   p.prefix_slots = (int)ceil_div64(max_blocks_per_seq, attn::kPrefixChunkBlocks);
   p.ws_bytes = (int64_t)num_seqs * H_q * (p.prefix_slots + p.n_split_max) * (attn::kDecodeHeadDim + 2) * 4;

@@ -113,6 +113,7 @@ constexpr int kDecodeBlockSize = 16;
 constexpr int kDecodeHeadDim = 128;
 int decode_split_blocks(int num_seqs, int H_kv, int max_blocks_per_seq);
 constexpr int kPrefixChunkBlocks = 32;  // prefix blocks per prefix-kernel workgroup
+constexpr int kDecodeSingleSplitPairs = 2048;  // shared-prefix decode: one split per sequence from here
 
 // Shared-prefix mode: the group gi of sequence s (group_start ascending,
 // group_start[0] = 0, group_start[num_groups] = num_seqs) and its shared

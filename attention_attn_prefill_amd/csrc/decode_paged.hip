@@ -30,7 +30,11 @@
 //   * the split's (max, sum, unnormalised o) go to the workspace, and a
 //     second kernel merges splits: M = max m_c, L = sum l_c 2^(m_c - M),
 //     O = sum o_c 2^(m_c - M) / L (scores are kept in the log2 domain).
-//     A sequence that fits one split is finished by the first kernel.
+//     A sequence that fits one split is finished by the first kernel;
+//   * shared-prefix mode (forked sequences): a sequence's splits start after
+//     its group's prefix blocks, whose partials the prefix kernel has
+//     written; with one split per sequence the split kernel folds them in
+//     itself, otherwise the merge kernel combines prefix and splits.
 #include "attn_internal.h"
 
 #include <math.h>
@@ -92,29 +96,40 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int cap = a.max_blocks_per_seq * BS;
   const bool len_bad = L_raw > cap;
   const int L = len_bad ? cap : L_raw;
-  // shared-prefix mode: the first `skip` blocks belong to the group's prefix
+  // shared-prefix mode: the first `skip` blocks belong to the group's
+  // prefix.  With one split per sequence this kernel also folds in the
+  // prefix partials and writes the output (no merge kernel); otherwise the
+  // merge kernel reports broken preconditions.
+  const bool shared_direct = a.group_start && a.n_split_max == 1;
   int skip = 0;
+  bool pre_bad = false;
   if (a.group_start) {
     int gi;
-    if (!decode_group_of(a, s, gi, skip)) return;  // reported by the merge
+    // the prefix must be valid and fit the sequence (whole visible blocks)
+    pre_bad = !decode_group_of(a, s, gi, skip) || skip * BS > L;
+    if (pre_bad && !shared_direct) return;
   }
   const int rem_blocks = (L + BS - 1) / BS - skip;
   const int n_split = (L > 0 && rem_blocks > 0) ? (rem_blocks + a.split_blocks - 1) / a.split_blocks : 0;
-  // this workgroup writes the final output (plain decode, one split)
-  const bool direct = n_split <= 1 && !a.group_start;
+  // this workgroup writes the final output (one split, or shared direct)
+  const bool direct = (n_split <= 1 && !a.group_start) || shared_direct;
 
-  if (L <= 0) {
-    // zero-length context: an all-zero row, written once (by the merge in
+  if (L <= 0 || (shared_direct && (pre_bad || len_bad))) {
+    // zero-length context: an all-zero row; a broken precondition in shared
+    // direct mode: NaN rows.  Written once (by the merge kernel in the other
     // shared-prefix mode)
-    if (split == 0 && !a.group_start) {
+    if (split == 0 && (!a.group_start || shared_direct)) {
+      const _Float16 fill = (_Float16)(L_raw <= 0 ? 0.0f : __builtin_nanf(""));
       for (int idx = tid; idx < G * D; idx += kThreads) {
         const int j = idx / D, d = idx - j * D;
-        a.out[((int64_t)s * a.H_q + g * G + j) * D + d] = (_Float16)0.0f;
+        a.out[((int64_t)s * a.H_q + g * G + j) * D + d] = fill;
       }
     }
     return;
   }
-  if (split >= n_split) return;  // empty split
+  // empty split (in shared direct mode split 0 runs even with no own
+  // blocks: the sequence is its prefix, and the output is still written here)
+  if (split >= (shared_direct ? 1 : n_split)) return;
 
   if (tid == 0) sm_bad = len_bad ? 1 : 0;
   __syncthreads();
@@ -255,6 +270,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     if (bad) {
       M = Ls = Os = __builtin_nanf("");
     }
+    if (shared_direct) {
+      // fold in the prefix chunks' partials (written by the prefix kernel
+      // earlier on the stream); a NaN partial keeps the row NaN
+      const int n_pre = (skip + kPrefixChunkBlocks - 1) / kPrefixChunkBlocks;
+      const int64_t base = ((int64_t)s * a.H_q + h) * a.slot_stride;
+      float Mt = M;
+      for (int c = 0; c < n_pre; ++c) Mt = fmaxf(Mt, a.ws_ml[(base + c) * 2]);
+      const float wown = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mt);
+      Ls *= wown;
+      Os *= wown;
+      for (int c = 0; c < n_pre; ++c) {
+        const float mc = a.ws_ml[(base + c) * 2];
+        const float w = (mc == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mc - Mt);
+        Ls = fmaf(a.ws_ml[(base + c) * 2 + 1], w, Ls);
+        Os = fmaf(a.ws_o[(base + c) * D + d], w, Os);
+      }
+    }
     if (direct) {
       a.out[((int64_t)s * a.H_q + h) * D + d] = (_Float16)(Os / Ls);
     } else {
@@ -318,7 +350,7 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   void* kargs[] = {&args};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<G>),
                                  dim3((unsigned)((int64_t)a.n_split_max * a.H_kv * a.num_seqs)), dim3(kThreads), kargs, 0, stream);
-  if (e != hipSuccess || (a.n_split_max <= 1 && !a.group_start)) return e;
+  if (e != hipSuccess || a.n_split_max <= 1) return e;  // one split: finished by the split kernel
   return hipLaunchKernel(reinterpret_cast<const void*>(&decode_merge_kernel),
                          dim3((unsigned)(a.num_seqs * a.H_q)), dim3(D), kargs, 0, stream);
 }

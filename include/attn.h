@@ -159,8 +159,11 @@ size_t attn_decode_paged_shared_prefix_workspace_size(int num_seqs, int H_q, int
  * Each group's prefix is attended once per kv head for all of its query
  * rows (group size x H_q/H_kv of them, in MFMA column blocks of 32), through
  * the table of the group's first sequence; every sequence's remaining blocks
- * go through the split-K decode kernel; a merge kernel combines the partial
- * results by log-sum-exp.  Three launches on `stream`.
+ * go through the split-K decode kernel, and the partial results are combined
+ * by log-sum-exp.  With num_seqs * H_kv >= 2048 every sequence's own blocks
+ * form one split that also combines the prefix partials (two launches on
+ * `stream`); below that, splits are shorter and a merge kernel combines
+ * them (three launches).
  *
  * workspace: at least attn_decode_paged_shared_prefix_workspace_size(...)
  * bytes (NULL or smaller is ATTN_ERR_WORKSPACE).

@@ -45,6 +45,8 @@ CASES = [  # group sizes, prompt lengths, suffix range, H_q, H_kv
     ([4, 4, 1], [2048, 16, 0], (1, 40), 8, 8),    # ratio 1; a group without a prefix
     ([6, 2], [640, 640], (0, 0), 32, 8),          # ratio 4; sequences that are only the prompt
     ([1] * 5, [100, 200, 300, 400, 500], (5, 50), 16, 2),  # singleton groups, ratio 8
+    ([8] * 4, [160] * 4, (1, 50), 16, 8),         # at most 16 blocks: one split, merged in the split kernel
+    ([4] * 64, [64, 80, 128, 0] * 16, (0, 300), 16, 8),  # 2048 (sequence, kv head) pairs: one split each
 ]
 
 
@@ -59,13 +61,16 @@ def test_shared_prefix_parity(sizes, prompts, suf, H_q, H_kv):
     assert_close_to_plain(got, gpu_decode(q, kc, vc, bt, sl))
 
 
-def test_preconditions_give_nan_or_zero_rows():
+@pytest.mark.parametrize("pad", [0, 40])
+def test_preconditions_give_nan_or_zero_rows(pad):
     """A prefix longer than one of the group's sequences, a bad prefix table
-    entry, and a zero-length sequence (prefix 0)."""
+    entry, and a zero-length sequence (prefix 0).  pad = 0: one split per
+    sequence (the split kernel writes the rows); pad = 40 unused table
+    columns: several splits and the merge kernel."""
     q, kc, vc, bt, sl, gs, pb = W.forked_decode_inputs([3, 3, 2], [64, 64, 32], [4, 9, 2, 1, 1, 1, 0, 5],
                                                        16, 8, seed=77)
     sl = sl.copy()
-    bt = bt.copy()
+    bt = np.concatenate([bt, np.full((bt.shape[0], pad), -1, np.int32)], axis=1)
     pb = pb.copy()
     sl[1] = 40                  # group 0: sequence 1 shorter than the 4-block prefix
     bt[3:6, 1] = kc.shape[0] + 5  # group 1: an out-of-pool prefix entry (all its tables)
