@@ -152,6 +152,7 @@ ATTN_EXPORT attn_status_t attn_decode_paged(const void* q, const void* k_cache, 
   a.n_split_max = plan.n_split_max;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
   a.group_start = nullptr;  // plain decode
+  a.seq_skip = nullptr;
   a.prefix_blocks = nullptr;
   a.num_groups = 0;
   a.max_group_size = 0;
@@ -179,7 +180,9 @@ static SharedPlan plan_shared(int num_seqs, int H_q, int H_kv, int max_blocks_pe
   if ((int64_t)num_seqs * H_kv >= attn::kDecodeSingleSplitPairs) p.split_blocks = max_blocks_per_seq;
   p.n_split_max = (int)ceil_div64(max_blocks_per_seq, p.split_blocks);
   p.prefix_slots = (int)ceil_div64(max_blocks_per_seq, attn::kPrefixChunkBlocks);
-  p.ws_bytes = (int64_t)num_seqs * H_q * (p.prefix_slots + p.n_split_max) * (attn::kDecodeHeadDim + 2) * 4;
+  // partial o and (max, sum) per slot, then the per-sequence prefix lengths
+  p.ws_bytes = (int64_t)num_seqs * H_q * (p.prefix_slots + p.n_split_max) * (attn::kDecodeHeadDim + 2) * 4 +
+               (int64_t)num_seqs * 4;
   return p;
 }
 
@@ -191,7 +194,7 @@ static attn_status_t check_shared(int num_seqs, int H_q, int H_kv, int head_dim,
     return ATTN_ERR_INVALID_ARG;
   const SharedPlan p = plan_shared(num_seqs, H_q, H_kv, max_blocks_per_seq);
   const int64_t col_blocks = ceil_div64((int64_t)max_group_size * (H_q / H_kv), 32);
-  if ((int64_t)p.prefix_slots * num_groups * H_kv * col_blocks > (int64_t)0x7fffffff ||
+  if ((int64_t)p.prefix_slots * num_groups * H_kv * col_blocks + ceil_div64(num_seqs, 256) > (int64_t)0x7fffffff ||
       (int64_t)p.n_split_max * H_kv * num_seqs > (int64_t)0x7fffffff)
     return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
@@ -236,6 +239,7 @@ ATTN_EXPORT attn_status_t attn_decode_paged_shared_prefix(
   const int64_t slots = (int64_t)num_seqs * H_q * (plan.prefix_slots + plan.n_split_max);
   a.ws_o = static_cast<float*>(workspace);
   a.ws_ml = a.ws_o + slots * attn::kDecodeHeadDim;
+  a.seq_skip = reinterpret_cast<int32_t*>(a.ws_ml + slots * 2);
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.H_q = H_q;

@@ -44,13 +44,17 @@ struct DecodeArgs {
   // group_start[i] .. group_start[i+1]-1 share their first prefix_blocks[i]
   // table entries.  Those blocks are attended once per group by the prefix
   // kernel (partials in slots [0, prefix_slots)); the split kernel covers the
-  // rest (slots prefix_slots + split); every row goes through the merge.
+  // rest (slots prefix_slots + split) and, with one split per sequence,
+  // folds in the prefix partials; otherwise the merge kernel does.
   const int32_t* group_start;
   const int32_t* prefix_blocks;
   int num_groups;
   int max_group_size;
   int prefix_slots;         // ceil(max_blocks_per_seq / kPrefixChunkBlocks), 0 when off
   int slot_stride;          // workspace slots per (sequence, query head)
+  // [num_seqs] (workspace): each sequence's prefix blocks, or -1 when its
+  // group breaks a checked rule; written by the prefix launch
+  int32_t* seq_skip;
 };
 
 struct KvAppendArgs {
@@ -135,6 +139,7 @@ __device__ __forceinline__ bool decode_group_of(const DecodeArgs& a, int s, int&
          a.group_start[lo + 1] <= a.num_seqs &&
          a.group_start[lo + 1] - a.group_start[lo] <= a.max_group_size;
 }
+// Prefix kernel plus, in the same launch, the per-sequence seq_skip table.
 hipError_t launch_decode_prefix(const DecodeArgs& a, int group, hipStream_t stream);
 
 }  // namespace attn

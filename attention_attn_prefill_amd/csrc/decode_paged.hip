@@ -104,10 +104,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   int skip = 0;
   bool pre_bad = false;
   if (a.group_start) {
-    int gi;
-    // the prefix must be valid and fit the sequence (whole visible blocks)
-    pre_bad = !decode_group_of(a, s, gi, skip) || skip * BS > L;
-    if (pre_bad && !shared_direct) return;
+    // the prefix must be valid (seq_skip >= 0) and fit the sequence
+    skip = a.seq_skip[s];
+    pre_bad = skip < 0 || skip * BS > L;
+    if (pre_bad) {
+      if (!shared_direct) return;
+      skip = 0;
+    }
   }
   const int rem_blocks = (L + BS - 1) / BS - skip;
   const int n_split = (L > 0 && rem_blocks > 0) ? (rem_blocks + a.split_blocks - 1) / a.split_blocks : 0;
@@ -273,18 +276,33 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     if (shared_direct) {
       // fold in the prefix chunks' partials (written by the prefix kernel
       // earlier on the stream); a NaN partial keeps the row NaN
+      // (four slots per round trip, combined online)
       const int n_pre = (skip + kPrefixChunkBlocks - 1) / kPrefixChunkBlocks;
       const int64_t base = ((int64_t)s * a.H_q + h) * a.slot_stride;
       float Mt = M;
-      for (int c = 0; c < n_pre; ++c) Mt = fmaxf(Mt, a.ws_ml[(base + c) * 2]);
-      const float wown = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mt);
-      Ls *= wown;
-      Os *= wown;
-      for (int c = 0; c < n_pre; ++c) {
-        const float mc = a.ws_ml[(base + c) * 2];
-        const float w = (mc == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mc - Mt);
-        Ls = fmaf(a.ws_ml[(base + c) * 2 + 1], w, Ls);
-        Os = fmaf(a.ws_o[(base + c) * D + d], w, Os);
+      for (int c0 = 0; c0 < n_pre; c0 += 4) {
+        float mc[4], lc[4], oc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool ok = c0 + u < n_pre;
+          const int64_t slot = base + (ok ? c0 + u : 0);
+          mc[u] = ok ? a.ws_ml[slot * 2] : -INFINITY;
+          lc[u] = ok ? a.ws_ml[slot * 2 + 1] : 0.0f;
+          oc[u] = ok ? a.ws_o[slot * D + d] : 0.0f;
+        }
+        float mn = Mt;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mn = fmaxf(mn, mc[u]);
+        const float wown = (Mt == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Mt - mn);
+        Ls *= wown;
+        Os *= wown;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = (mc[u] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mc[u] - mn);
+          Ls = fmaf(lc[u], w, Ls);
+          Os = fmaf(oc[u], w, Os);
+        }
+        Mt = mn;
       }
     }
     if (direct) {
@@ -317,9 +335,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
       *dst = (_Float16)0.0f;
       return;
     }
-    int gi;
-    // the prefix must fit the sequence (whole blocks of visible tokens)
-    if (!decode_group_of(a, s, gi, skip) || L_raw > cap || skip * BS > L) {
+    // the prefix must be valid and fit the sequence (whole visible blocks)
+    skip = a.seq_skip[s];
+    if (skip < 0 || L_raw > cap || skip * BS > L) {
       *dst = (_Float16)__builtin_nanf("");
       return;
     }

@@ -106,6 +106,17 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a,
   static_assert(kStages == 4, "wait_tiles covers up to two tiles in flight behind the current one");
   // block id -> (chunk, group, kv head, column block), chunk slowest
   const int per_chunk = a.num_groups * a.H_kv * col_blocks;
+  const int main_blocks = a.prefix_slots * per_chunk;
+  if ((int)blockIdx.x >= main_blocks) {
+    // the trailing workgroups record every sequence's prefix length (or -1
+    // when its group breaks a checked rule) for the split and merge kernels
+    const int s = ((int)blockIdx.x - main_blocks) * (64 * kWaves) + (int)threadIdx.x;
+    if (s < a.num_seqs) {
+      int gi, skip;
+      a.seq_skip[s] = decode_group_of(a, s, gi, skip) ? skip : -1;
+    }
+    return;
+  }
   const int chunk = blockIdx.x / per_chunk;
   int rest = blockIdx.x - chunk * per_chunk;
   const int cb = rest % col_blocks;
@@ -276,7 +287,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a,
 template <int G>
 hipError_t launch_prefix_g(const DecodeArgs& a, hipStream_t stream) {
   const int col_blocks = (a.max_group_size * G + 31) / 32;
-  const int64_t blocks = (int64_t)a.prefix_slots * a.num_groups * a.H_kv * col_blocks;
+  const int64_t blocks = (int64_t)a.prefix_slots * a.num_groups * a.H_kv * col_blocks +
+                        (a.num_seqs + 64 * kWaves - 1) / (64 * kWaves);
   DecodeArgs args = a;
   int cbs = col_blocks;
   void* kargs[] = {&args, &cbs};
