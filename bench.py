@@ -6,6 +6,9 @@ block_size=16, seq_lens uniform in [128, 4096], permuted block tables) --
 the Qwen3-0.6B-shaped workloads, both entry points of the C ABI, on synthetic
 seeded inputs already resident in HBM.  ``--workload long`` swaps in the
 long-context pair (prefill B=1 S=32768; decode 64 x 32768 tokens).
+``--workload grpo`` times only the shared-prefix decode of forked sequences
+(32 prompts of 2048 tokens, 8 samples each with U[1, 512] tokens of their
+own), which the default line also carries as ``shared_prefix_decode``.
 
 Prints one JSON line.  ``value`` is prefill TFLOP/s (exact unmasked-pair flop
 count, 4*D per pair); the decode half of the metric (KV GB/s: K and V bytes
@@ -36,11 +39,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", choices=["qwen3", "long"], default="qwen3")
+    p.add_argument("--workload", choices=["qwen3", "long", "grpo"], default="qwen3")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile", action="store_true",
                    help="counter runs: no CPU baseline, and first a plain 512 MiB fp16 "
-                        "negation (reads and writes 512 MiB) to calibrate the byte counters")
+                        "negation (reads and writes 512 MiB) to calibrate the byte counters; "
+                        "no shared-prefix leg (its kernels share names with plain decode), "
+                        "and with --workload grpo only the shared-prefix calls")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle sample")
     return p.parse_args()
@@ -54,6 +59,8 @@ KERNEL_SOURCES = {
     "kv_append_kernel": ["attention_attn_prefill_amd/csrc/kv_append.hip",
                          "attention_attn_prefill_amd/csrc/attn_internal.h"],
     "qk_norm_rope_kernel": ["attention_attn_prefill_amd/csrc/rope_norm.hip",
+                            "attention_attn_prefill_amd/csrc/attn_internal.h"],
+    "prefix_chunk_kernel": ["attention_attn_prefill_amd/csrc/decode_prefix.hip",
                             "attention_attn_prefill_amd/csrc/attn_internal.h"],
 }
 
@@ -256,7 +263,7 @@ def time_cross_module(dev, stream, W, iters=200):
                          "frac": round(tf / PEAK_FP16_TFLOPS, 5)}}
 
 
-def time_shared_prefix(dev, stream, W, iters=50):
+def time_shared_prefix(dev, stream, W, iters=50, shared_only=False):
     """The forked-decode workload (32 prompts of 2048 tokens, 8 samples each
     with U[1, 512] tokens of their own; H 16/8, D 128): plain paged decode
     against the shared-prefix path on the same tables.  Logical KV bytes count
@@ -297,20 +304,59 @@ def time_shared_prefix(dev, stream, W, iters=50):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters
 
-    ms_plain, ms_shared = timed(plain), timed(shared)
+    ms_plain = None if shared_only else timed(plain)
+    ms_shared = timed(shared)
     row = Hkv * D * 2 * 2  # K + V bytes per token
     logical = int(sl.astype(np.int64).sum()) * row
     shared_tokens = int(np.sum(pb.astype(np.int64) * 16 * (np.diff(gs) - 1)))
     unique = logical - shared_tokens * row
     return {"metric": "forked paged decode: logical KV GB/s", "value": round(logical / (ms_shared * 1e-3) / 1e9, 1),
-            "unit": "GB/s", "launch_ms": round(ms_shared, 5), "plain_decode_ms": round(ms_plain, 5),
-            "speedup_vs_plain_decode": round(ms_plain / ms_shared, 3),
+            "unit": "GB/s", "launch_ms": round(ms_shared, 5),
+            "plain_decode_ms": None if ms_plain is None else round(ms_plain, 5),
+            "speedup_vs_plain_decode": None if ms_plain is None else round(ms_plain / ms_shared, 3),
             "logical_kv_bytes": logical, "unique_kv_bytes": unique,
             "config": dict(c),
-            "roofline": {"bound": "hbm", "kernel": "prefix_chunk_kernel + decode_split_kernel + decode_merge_kernel",
+            "roofline": {"bound": "hbm", "kernel": "prefix_chunk_kernel + decode_split_kernel (one split per sequence)",
                          "achieved": round(unique / (ms_shared * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s (unique bytes)",
-                         "frac": round(unique / (ms_shared * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+                         "frac": round(unique / (ms_shared * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": shared_traffic(),
+                         "traffic_unit": "bytes per call (HBM read + write, rocprofv3 counters, both kernels)"}}
+
+
+def shared_traffic():
+    """HBM bytes per shared-prefix call: prefix kernel plus shared-mode split
+    kernel, from profiles/hbm_traffic_grpo.md (None if either is stale)."""
+    a = measured_traffic("grpo", "prefix_chunk_kernel")
+    b = measured_traffic("grpo", "decode_split_kernel")
+    return None if a is None or b is None else a + b
+
+
+def main_grpo(args):
+    import torch
+
+    from attention_attn_prefill_amd import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    if args.profile:
+        calibration_copy(dev)
+    leg = time_shared_prefix(dev, stream, W, iters=args.steps, shared_only=args.profile)
+    leg.update({"n_gpus": 1, "steps": args.steps, "warmup": 10, "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "f16 (fp32 accumulate)",
+                "data": "synthetic, seeded N(0,1) fp16; forked block tables (shared prompt blocks)"})
+    leg["config"] = {"workload": "grpo_decode: 32 prompts x 8 samples, prompt 2048 tokens, own tokens U[1,512], "
+                                 "H_q=16 H_kv=8 D=128 block_size=16", **leg["config"]}
+    print(json.dumps(leg), flush=True)
+
+
+def calibration_copy(dev):
+    import torch
+    src = torch.ones(256 << 20, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    print("[bench] calibration copy: 512 MiB read + 512 MiB written", file=sys.stderr, flush=True)
 
 
 def main():
@@ -319,6 +365,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "grpo":
+        main_grpo(args)
+        return
 
     import torch
 
@@ -347,12 +397,7 @@ def main():
     print("[bench] inputs resident in HBM", file=sys.stderr, flush=True)
     if args.profile:
         args.no_cpu_baseline = True
-        src = torch.ones(256 << 20, dtype=torch.float16, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-        print("[bench] calibration copy: 512 MiB read + 512 MiB written", file=sys.stderr, flush=True)
+        calibration_copy(dev)
 
     def step(ev=None):
         if ev is not None:
@@ -435,7 +480,8 @@ def main():
     line["kv_append"] = time_kv_append(pcfg, k, v, dev, stream, W, traffic_key)
     line["qk_norm_rope_append"] = time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key)
     line["cross_attention_module"] = time_cross_module(dev, stream, W)
-    line["shared_prefix_decode"] = time_shared_prefix(dev, stream, W)
+    if not args.profile:
+        line["shared_prefix_decode"] = time_shared_prefix(dev, stream, W)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl,
