@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     attn_decode_paged_workspace_size,
     attn_kv_append,
     attn_prefill,
+    attn_prefill_qk_norm_rope,
     attn_qk_norm_rope,
     attn_qk_norm_rope_append,
     attn_rope_table,

@@ -38,19 +38,21 @@ def load_library():
             "(python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    F, D_ = ctypes.c_float, ctypes.c_double
     lib.attn_abi_version.argtypes = []
     lib.attn_abi_version.restype = I
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P]
     lib.attn_prefill.restype = I
+    lib.attn_prefill_qk_norm_rope.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.attn_prefill_qk_norm_rope.restype = I
     lib.attn_decode_paged_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_paged_workspace_size.restype = SZ
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I64, P, SZ, P]
     lib.attn_decode_paged.restype = I
     lib.attn_kv_append.argtypes = [P, P, P, P, P, I64, I, I, I, I64, P]
     lib.attn_kv_append.restype = I
-    F, D_ = ctypes.c_float, ctypes.c_double
     lib.attn_rope_table.argtypes = [P, P, I, I, D_, P]
     lib.attn_rope_table.restype = I
     lib.attn_qk_norm_rope.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I, F, P]
@@ -114,6 +116,35 @@ def attn_prefill(q, k, v, o, causal: bool = True, stream=None) -> None:
                                      _stream_handle(stream, q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_prefill")
+
+
+def attn_prefill_qk_norm_rope(q, k, v, o, q_weight, cos_table, sin_table, positions, eps: float = 1e-6,
+                              causal: bool = True, stream=None) -> None:
+    """Prefill with the query QK-norm + NeoX RoPE fused into the query load
+    via ``attn_prefill_qk_norm_rope``: q [B,S_q,H_q,D] is read only, q_weight
+    [D] fp16 or None, fp32 tables [max_pos, D/2], int32 positions [B*S_q]
+    or None (row i of every sequence at position i); k must already be
+    normalised and rotated."""
+    import torch
+    B, S_q, H_q, D = q.shape
+    S_kv, H_kv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, S_kv, H_kv, D) or tuple(v.shape) != tuple(k.shape) or \
+            tuple(o.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k, v, o")
+    if cos_table.dim() != 2 or cos_table.shape[1] != D // 2 or \
+            tuple(sin_table.shape) != tuple(cos_table.shape) or \
+            (positions is not None and positions.numel() != B * S_q):
+        raise ValueError("tables must be [max_pos, head_dim/2] and positions [B*S_q] or None")
+    if q_weight is not None and q_weight.numel() != D:
+        raise ValueError("q_weight must have head_dim elements")
+    args = [_dev_tensor(x, torch.float16, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    args += [ctypes.c_void_p(None) if q_weight is None else _dev_tensor(q_weight, torch.float16, "q_weight"),
+             _dev_tensor(cos_table, torch.float32, "cos_table"), _dev_tensor(sin_table, torch.float32, "sin_table"),
+             ctypes.c_void_p(None) if positions is None else _dev_tensor(positions, torch.int32, "positions")]
+    st = load_library().attn_prefill_qk_norm_rope(*args, B, S_q, S_kv, H_q, H_kv, D, cos_table.shape[0],
+                                                  float(eps), int(bool(causal)), _stream_handle(stream, q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_prefill_qk_norm_rope")
 
 
 def attn_decode_paged_workspace_size(num_seqs: int, H_q: int, H_kv: int, head_dim: int,
@@ -196,25 +227,31 @@ def attn_rope_table(cos_table, sin_table, theta: float, stream=None) -> None:
 
 
 def _rope_args(q, k, q_weight, k_weight, cos_table, sin_table, positions):
+    """Pointers and sizes of the QK-norm + RoPE entry points; q None is the
+    K-only form (then q_weight must be None and H_q is passed as 1)."""
     import torch
-    H_q, D = q.shape[-2], q.shape[-1]
-    H_kv = k.shape[-2]
-    num_tokens = q.numel() // (H_q * D)
-    if k.shape[-1] != D or k.numel() != num_tokens * H_kv * D or positions.numel() != num_tokens:
+    D, H_kv = k.shape[-1], k.shape[-2]
+    if q is None:
+        if q_weight is not None:
+            raise ValueError("q_weight needs q")
+        H_q, num_tokens = 1, k.numel() // (H_kv * D)
+    else:
+        H_q = q.shape[-2]
+        num_tokens = q.numel() // (H_q * D)
+        if q.shape[-1] != D or (q_weight is None) != (k_weight is None):
+            raise ValueError("q/k head_dim differ, or only one of q_weight / k_weight is given")
+    if k.numel() != num_tokens * H_kv * D or positions.numel() != num_tokens:
         raise ValueError("q, k and positions disagree on num_tokens / head_dim")
     if cos_table.dim() != 2 or cos_table.shape[1] != D // 2 or \
             tuple(sin_table.shape) != tuple(cos_table.shape):
         raise ValueError("tables must be [max_pos, head_dim/2]")
-    if (q_weight is None) != (k_weight is None):
-        raise ValueError("q_weight and k_weight must both be given or both be None")
-    ptrs = [_dev_tensor(q, torch.float16, "q"), _dev_tensor(k, torch.float16, "k")]
-    if q_weight is None:
-        ptrs += [ctypes.c_void_p(None), ctypes.c_void_p(None)]
-    else:
-        if q_weight.numel() != D or k_weight.numel() != D:
+    for w in (q_weight, k_weight):
+        if w is not None and w.numel() != D:
             raise ValueError("weights must have head_dim elements")
-        ptrs += [_dev_tensor(q_weight, torch.float16, "q_weight"),
-                 _dev_tensor(k_weight, torch.float16, "k_weight")]
+    none = ctypes.c_void_p(None)
+    ptrs = [none if q is None else _dev_tensor(q, torch.float16, "q"), _dev_tensor(k, torch.float16, "k"),
+            none if q_weight is None else _dev_tensor(q_weight, torch.float16, "q_weight"),
+            none if k_weight is None else _dev_tensor(k_weight, torch.float16, "k_weight")]
     ptrs += [_dev_tensor(cos_table, torch.float32, "cos_table"),
              _dev_tensor(sin_table, torch.float32, "sin_table"),
              _dev_tensor(positions, torch.int32, "positions")]
@@ -226,6 +263,8 @@ def attn_qk_norm_rope(q, k, q_weight, k_weight, cos_table, sin_table, positions,
     """In place: per-head RMSNorm (weights [D] fp16, or both None) then the
     NeoX rotation of q [..., H_q, D] and k [..., H_kv, D] at int32 positions
     [num_tokens], via ``attn_qk_norm_rope``."""
+    if q is None:
+        raise ValueError("attn_qk_norm_rope needs q (the K-only form is attn_qk_norm_rope_append)")
     ptrs, n, H_q, H_kv, D, max_pos = _rope_args(q, k, q_weight, k_weight, cos_table, sin_table,
                                                 positions)
     st = load_library().attn_qk_norm_rope(*ptrs, n, H_q, H_kv, D, max_pos, float(eps),
@@ -239,7 +278,8 @@ def attn_qk_norm_rope_append(q, k, v, q_weight, k_weight, cos_table, sin_table, 
     """attn_qk_norm_rope, and in the same pass the rotated k rows and the v
     rows [..., H_kv, D] go to the paged caches [num_blocks, H_kv, block_size, D]
     at int64 slot_mapping [num_tokens] (-1 skipped), via
-    ``attn_qk_norm_rope_append``."""
+    ``attn_qk_norm_rope_append``.  q = None (with q_weight None): keys and
+    values only, for ``attn_prefill_qk_norm_rope``."""
     import torch
     ptrs, n, H_q, H_kv, D, max_pos = _rope_args(q, k, q_weight, k_weight, cos_table, sin_table,
                                                 positions)
@@ -256,7 +296,7 @@ def attn_qk_norm_rope_append(q, k, v, q_weight, k_weight, cos_table, sin_table, 
     args = ptrs[:2] + [vp] + ptrs[2:]
     st = load_library().attn_qk_norm_rope_append(*args, n, H_q, H_kv, D, max_pos, float(eps), kc, vc,
                                                  sm, block_size, num_blocks,
-                                                 _stream_handle(stream, q.device))
+                                                 _stream_handle(stream, k.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_qk_norm_rope_append")
 

@@ -67,9 +67,9 @@ ATTN_EXPORT const char* attn_status_string(attn_status_t status) {
   return "ATTN_ERR_UNKNOWN";
 }
 
-ATTN_EXPORT attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o, int B,
-                                       int S_q, int S_kv, int H_q, int H_kv, int head_dim,
-                                       int causal, void* stream) {
+static attn_status_t prefill_args(const void* q, const void* k, const void* v, void* o, int B, int S_q,
+                                  int S_kv, int H_q, int H_kv, int head_dim, int causal,
+                                  attn::PrefillArgs& a) {
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
   if (B <= 0 || S_q <= 0 || S_kv <= 0 || H_q <= 0 || H_kv <= 0 || head_dim <= 0)
     return ATTN_ERR_INVALID_ARG;
@@ -83,7 +83,6 @@ ATTN_EXPORT attn_status_t attn_prefill(const void* q, const void* k, const void*
   // K/V rows of one batch entry are addressed with 32-bit byte offsets
   if ((int64_t)S_kv * H_kv * head_dim * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
 
-  attn::PrefillArgs a;
   a.q = static_cast<const _Float16*>(q);
   a.k = static_cast<const _Float16*>(k);
   a.v = static_cast<const _Float16*>(v);
@@ -95,6 +94,39 @@ ATTN_EXPORT attn_status_t attn_prefill(const void* q, const void* k, const void*
   a.H_kv = H_kv;
   a.n_qtiles = 0;  // set by the launcher
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  return ATTN_OK;
+}
+
+ATTN_EXPORT attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o, int B,
+                                       int S_q, int S_kv, int H_q, int H_kv, int head_dim,
+                                       int causal, void* stream) {
+  attn::PrefillArgs a;
+  const attn_status_t st = prefill_args(q, k, v, o, B, S_q, S_kv, H_q, H_kv, head_dim, causal, a);
+  if (st != ATTN_OK) return st;
+  const hipError_t e = attn::launch_prefill(a, head_dim, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_EXPORT attn_status_t attn_prefill_qk_norm_rope(const void* q, const void* k, const void* v, void* o,
+                                                    const void* q_weight, const float* cos_table,
+                                                    const float* sin_table, const int32_t* positions,
+                                                    int B, int S_q, int S_kv, int H_q, int H_kv,
+                                                    int head_dim, int max_pos, float eps, int causal,
+                                                    void* stream) {
+  attn::PrefillArgs a;
+  const attn_status_t st = prefill_args(q, k, v, o, B, S_q, S_kv, H_q, H_kv, head_dim, causal, a);
+  if (st != ATTN_OK) return st;
+  if (!cos_table || !sin_table || max_pos <= 0 || !(eps >= 0.0f)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(cos_table, 16) || !aligned(sin_table, 16) || (positions && !aligned(positions, 4)) ||
+      (q_weight && !aligned(q_weight, 16)))
+    return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)max_pos * (head_dim / 2) >= ((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+  a.q_weight = static_cast<const _Float16*>(q_weight);
+  a.cos_table = cos_table;
+  a.sin_table = sin_table;
+  a.positions = positions;
+  a.max_pos = max_pos;
+  a.eps = eps;
   const hipError_t e = attn::launch_prefill(a, head_dim, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -309,10 +341,12 @@ static attn_status_t qk_norm_rope_common(void* q, void* k, const void* v, const 
     return ATTN_ERR_INVALID_ARG;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (num_tokens == 0) return ATTN_OK;  // nothing is read or written
-  if (!q || !k || !cos_table || !sin_table || !positions) return ATTN_ERR_INVALID_ARG;
-  if ((q_weight == nullptr) != (k_weight == nullptr)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(cos_table, 16) || !aligned(sin_table, 16) ||
-      !aligned(positions, 4) || (q_weight && (!aligned(q_weight, 16) || !aligned(k_weight, 16))))
+  // q may be null when appending (K-only: Q is rotated by the prefill that
+  // reads it); then q_weight must be null too
+  if ((!q && !append) || !k || !cos_table || !sin_table || !positions) return ATTN_ERR_INVALID_ARG;
+  if (q ? (q_weight == nullptr) != (k_weight == nullptr) : q_weight != nullptr) return ATTN_ERR_INVALID_ARG;
+  if ((q && !aligned(q, 16)) || !aligned(k, 16) || !aligned(cos_table, 16) || !aligned(sin_table, 16) ||
+      !aligned(positions, 4) || (q_weight && !aligned(q_weight, 16)) || (k_weight && !aligned(k_weight, 16)))
     return ATTN_ERR_INVALID_ARG;
   if (append) {
     if (!v || !k_cache || !v_cache || !slot_mapping || block_size <= 0 || num_blocks <= 0)
@@ -321,7 +355,7 @@ static attn_status_t qk_norm_rope_common(void* q, void* k, const void* v, const 
       return ATTN_ERR_INVALID_ARG;
   }
   const int64_t rows_per_block = (64 / (head_dim / 8)) * 4;
-  const int64_t heads = (int64_t)H_q + (int64_t)H_kv * (append ? 2 : 1);
+  const int64_t heads = (q ? (int64_t)H_q : 0) + (int64_t)H_kv * (append ? 2 : 1);
   if (num_tokens > ((int64_t)1 << 40) / heads ||
       ceil_div64(num_tokens * heads, rows_per_block) > (int64_t)0x7fffffff)
     return ATTN_ERR_UNSUPPORTED;

@@ -23,6 +23,14 @@ struct PrefillArgs {
   int B, S_q, S_kv, H_q, H_kv;
   int n_qtiles;      // ceil(S_q / BLOCK_M)
   float scale_log2;  // log2(e) / sqrt(D)
+  // Optional per-head RMSNorm + NeoX rotation of Q as it is loaded (off when
+  // cos_table is null): Q row (b, i) turns by the table row positions[b*S_q+i].
+  const _Float16* q_weight = nullptr;  // [D] or null (rotation only)
+  const float* cos_table = nullptr;    // [max_pos, D/2]
+  const float* sin_table = nullptr;
+  const int32_t* positions = nullptr;  // [B * S_q], or null: row i of each sequence is at i
+  int max_pos = 0;
+  float eps = 0.0f;
 };
 
 struct DecodeArgs {

@@ -44,6 +44,7 @@ constexpr int BS = kDecodeBlockSize;  // 16
 constexpr int CB = kPrefixChunkBlocks;
 constexpr int kStages = 4;
 constexpr int kTileHalfs = 32 * D;    // one 32-key tile of K or V
+static_assert(CB % 2 == 0 && CB <= 64, "a chunk is whole 2-block tiles, its table entries one per lane");
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -93,17 +94,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const _Float16* p) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, BS * D * 2, 0x00020000);
 }
 
-template <int kOutstanding>
-__device__ __forceinline__ void wait_tiles() {
-  // each tile costs every lane 4 buffer-to-LDS loads
-  if constexpr (kOutstanding == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (kOutstanding == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  if constexpr (kOutstanding == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+// Wait until at most `ahead` tiles (4 buffer-to-LDS loads per lane each)
+// are still in flight behind the current one.
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  static_assert(kStages >= 2 && kStages <= 8, "vmcnt immediates below cover up to six tiles ahead");
+  switch (ahead) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+  }
 }
 
 template <int G>
 __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a, int col_blocks) {
-  static_assert(kStages == 4, "wait_tiles covers up to two tiles in flight behind the current one");
   // block id -> (chunk, group, kv head, column block), chunk slowest
   const int per_chunk = a.num_groups * a.H_kv * col_blocks;
   const int main_blocks = a.prefix_slots * per_chunk;
@@ -210,10 +217,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a,
     if (t < n_tiles) issue(t);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int ahead = n_tiles - 1 - t;
-    if (ahead >= 2) wait_tiles<2>();
-    else if (ahead == 1) wait_tiles<1>();
-    else wait_tiles<0>();
+    wait_tiles(min(kStages - 2, n_tiles - 1 - t));
     // tile t is in LDS for every wavefront, and every wavefront is done
     // with tile t - 1, whose stage is refilled next.  A bare barrier: the
     // waits it needs are explicit (the loads' vmcnt above; every LDS read of

@@ -38,7 +38,15 @@
 //     crossing the diagonal (or the ragged end) are masked element-wise;
 //   * a workgroup runs query tiles i and n-1-i back to back: under the causal
 //     mask every such pair costs the same, so the grid has no tail of long
-//     tiles (an odd middle tile runs alone, last).
+//     tiles (an odd middle tile runs alone, last);
+//   * optionally (ROPE) Q gets the Qwen3 per-head RMSNorm and NeoX rotation
+//     as it is loaded ("GRPO-CUDA Project Memory", Qwen3 notes and "RoPE
+//     design"), in fp32, rounded to fp16 once: a lane holds dims
+//     16ks + 8hf + (0..7), so the split-half partner of dim d < D/2 (d + D/2,
+//     k-step ks + KS/2) is in the same lane, and the mean square needs one
+//     swap with lane l ^ 32, which holds the rest of the row.  Q is read
+//     once per wavefront, so this costs nothing next to the tile loop;
+//     K is rotated once, by the pass that also writes it to the cache.
 #include "attn_internal.h"
 
 #include <math.h>
@@ -198,6 +206,90 @@ __device__ __forceinline__ void qk_tile(f32x16_t (&s)[2], const _Float16* kl, co
   }
 }
 
+// RMSNorm (when q_weight is set) and NeoX rotation of the Q fragment of one
+// lane (dims 16 ks + 8 hf + j of its query row), in fp32, rounded to fp16
+// once.  Its loads go out in two waves so that their latency overlaps the
+// first K/V tile loads: the weight slices and the position with the Q loads
+// (issue), the table rows once the position is known (tables), then the
+// arithmetic (apply).  Without a positions array the position is the row's
+// index in its sequence and the table rows go out with the Q loads too.  Rows past S_q stay zero.  apply() returns false for a
+// position outside [0, max_pos): that row's fragment is zero (this file is
+// built without NaN semantics, so no NaN enters the arithmetic) and the
+// epilogue stores NaN bits for it.  Every lane of the wavefront takes part
+// in apply() (the row sum is exchanged with lane l ^ 32).
+template <int D>
+struct QNormRope {
+  static constexpr int KS = D / 16, HK = KS / 2;
+  half8_t w[KS];
+  f32x4_t c[HK][2], s[HK][2];
+  int pos;
+  bool valid, ok;
+
+  __device__ __forceinline__ void issue(const PrefillArgs& a, int b, int qrow, int hf) {
+    valid = qrow < a.S_q;
+    if (a.positions) {
+      pos = valid ? a.positions[(int64_t)b * a.S_q + qrow] : 0;
+    } else {
+      pos = qrow;
+      tables(a, hf);
+    }
+    if (a.q_weight) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const half8_t*>(a.q_weight + 16 * ks + 8 * hf);
+    }
+  }
+  __device__ __forceinline__ void tables(const PrefillArgs& a, int hf) {
+    ok = pos >= 0 && pos < a.max_pos;
+    const int64_t trow = (int64_t)(ok ? pos : 0) * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < HK; ++ks) {
+      const f32x4_t* ct = reinterpret_cast<const f32x4_t*>(a.cos_table + trow + 16 * ks + 8 * hf);
+      const f32x4_t* st = reinterpret_cast<const f32x4_t*>(a.sin_table + trow + 16 * ks + 8 * hf);
+      c[ks][0] = ct[0];
+      c[ks][1] = ct[1];
+      s[ks][0] = st[0];
+      s[ks][1] = st[1];
+    }
+  }
+  __device__ __forceinline__ bool apply(const PrefillArgs& a, half8_t (&qf)[KS]) const {
+    float y[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[ks][j] = (float)qf[ks][j];
+    if (a.q_weight) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(y[ks][j], y[ks][j], ss);
+      ss = wave_half_swap_add(ss);
+      // v_rsq_f32 directly: the math library's rsqrtf is not inlined into
+      // this file (built without NaN semantics) and would become a call; for
+      // the normal arguments a mean square plus eps gives, it is the same
+      // instruction
+      const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[ks][j] = y[ks][j] * inv * (float)w[ks][j];
+    }
+#pragma unroll
+    for (int ks = 0; ks < HK; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float cj = c[ks][j >> 2][j & 3], sj = s[ks][j >> 2][j & 3];
+        const float lo = y[ks][j], hi = y[ks + HK][j];
+        const float rlo = fmaf(lo, cj, -hi * sj);
+        const float rhi = fmaf(hi, cj, lo * sj);
+        qf[ks][j] = (valid && ok) ? (_Float16)rlo : (_Float16)0.0f;
+        qf[ks + HK][j] = (valid && ok) ? (_Float16)rhi : (_Float16)0.0f;
+      }
+    }
+    return !valid || ok;
+  }
+};
+
 // All per-wavefront state of one prefill workgroup, and the per-tile step.
 template <int D, bool CAUSAL, int HP>
 struct Prefill {
@@ -317,7 +409,7 @@ struct Prefill {
 
 // One query tile (128 rows of each of the HP heads of head group hg, batch b)
 // against its keys, from the first K/V tile to the last.
-template <int D, bool CAUSAL, int HP>
+template <int D, bool CAUSAL, int HP, bool ROPE>
 __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int hg, int b,
                                               _Float16* k_lds, _Float16* vt_lds) {
 
@@ -326,7 +418,7 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
   P p;
   p.k_lds = k_lds;
   p.vt_lds = vt_lds;
-  p.tid = threadIdx.x;
+  p.tid = (int)__builtin_amdgcn_workitem_id_x();  // threadIdx.x (see the kernel)
   const int lane = p.tid & 63;
   const int wave = p.tid >> 6;
   const int col = lane & 31;  // query column of S^T / O^T owned by this lane
@@ -351,6 +443,9 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
 #pragma unroll
     for (int ks = 0; ks < P::KS; ++ks) p.qf[ks] = half8_t{};
   }
+  // the row's position and the norm weights go out with the Q loads
+  QNormRope<D> qr;
+  if constexpr (ROPE) qr.issue(a, b, p.qrow, p.hf);
 #pragma unroll
   for (int dt = 0; dt < P::DT; ++dt) p.o[dt] = f32x16_t{};
   p.m = -INFINITY;  // reference point of the exponentials (raw dot-product units)
@@ -378,8 +473,13 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
 
   // prologue: K(0), V(0) and K(1) into LDS
   p.st.init(p.kbase, p.vbase, (int)p.kv_row_stride, a.S_kv);
+  if constexpr (ROPE) {
+    if (a.positions) qr.tables(a, p.hf);  // as soon as the position is in
+  }
   p.st.load_k(0, p.tid);
   p.st.load_v(0, p.tid);
+  bool q_ok = true;
+  if constexpr (ROPE) q_ok = qr.apply(a, p.qf);
   p.st.store_k(k_lds, p.tid);
   p.st.store_v(vt_lds, p.tid);
   if (n_tiles > 1) {
@@ -421,6 +521,7 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
       half4_t out;
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[j] = (_Float16)(p.o[dt][rg * 4 + j] * inv);
+      if (ROPE && !q_ok) out = __builtin_bit_cast(half4_t, 0x7e007e007e007e00ull);  // quiet NaN bits
       *reinterpret_cast<half4_t*>(op + dt * 32 + rg * 8 + p.hf * 4) = out;
     }
   }
@@ -430,7 +531,7 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
 // group, batch).  Under the causal mask tile i costs i+1 units of 128 keys,
 // so every pair costs the same n_qtiles+1 units and the grid has no
 // long-tile tail; an odd middle tile runs alone, after all pairs.
-template <int D, bool CAUSAL, int HP>
+template <int D, bool CAUSAL, int HP, bool ROPE>
 __global__ __launch_bounds__(64 * kWavesPerHead * HP, 2) void prefill_fwd_kernel(PrefillArgs a) {
   using P = Prefill<D, CAUSAL, HP>;
   // K runs one tile ahead of V: at step t the math reads K(t+1) and V(t)
@@ -439,32 +540,37 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, 2) void prefill_fwd_kernel
 
   const int head_groups = a.H_q / HP;
   const int combos = head_groups * a.B;
-  const int id = blockIdx.x;
+  // The raw work-group / work-item id builtins: this file is built without NaN
+  // semantics, so the device library's blockIdx / threadIdx helpers (built
+  // with them) are not inlined and would become calls.
+  const int id = (int)__builtin_amdgcn_workgroup_id_x();
   const int pair = id / combos;
   const int rem = id - pair * combos;
   const int hg = rem % head_groups;
   const int b = rem / head_groups;
   const int lo = pair, hi = a.n_qtiles - 1 - pair;
-  prefill_qtile<D, CAUSAL, HP>(a, hi, hg, b, k_lds, vt_lds);
+  prefill_qtile<D, CAUSAL, HP, ROPE>(a, hi, hg, b, k_lds, vt_lds);
   if (lo < hi) {
     __syncthreads();  // the first tile's last LDS reads are done
-    prefill_qtile<D, CAUSAL, HP>(a, lo, hg, b, k_lds, vt_lds);
+    prefill_qtile<D, CAUSAL, HP, ROPE>(a, lo, hg, b, k_lds, vt_lds);
   }
 }
 
-template <int D, bool CAUSAL, int HP>
+template <int D, bool CAUSAL, int HP, bool ROPE>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)((a.n_qtiles + 1) / 2) * (a.H_q / HP) * a.B;
   PrefillArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_fwd_kernel<D, CAUSAL, HP>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_fwd_kernel<D, CAUSAL, HP, ROPE>),
                          dim3((unsigned)blocks), dim3(64 * kWavesPerHead * HP), kargs, 0, stream);
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_hp(const PrefillArgs& a, hipStream_t stream) {
   const bool pair = ((a.H_q / a.H_kv) % 2) == 0;
-  return pair ? launch_t<D, CAUSAL, 2>(a, stream) : launch_t<D, CAUSAL, 1>(a, stream);
+  if (a.cos_table)
+    return pair ? launch_t<D, CAUSAL, 2, true>(a, stream) : launch_t<D, CAUSAL, 1, true>(a, stream);
+  return pair ? launch_t<D, CAUSAL, 2, false>(a, stream) : launch_t<D, CAUSAL, 1, false>(a, stream);
 }
 
 }  // namespace

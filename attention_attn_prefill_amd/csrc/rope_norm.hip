@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(RopeArgs a) {
   const int sub = lane % LPR;          // which 8-element slice of the row
   const int64_t row = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6) * RPW + lane / LPR;
 
-  const int64_t rq = a.num_tokens * a.H_q;
+  const int64_t rq = a.q ? a.num_tokens * a.H_q : 0;  // no q rows in K-only mode
   const int64_t rk = a.num_tokens * a.H_kv;
   const int64_t total = rq + rk + (APPEND ? rk : 0);
   if (row >= total) return;  // whole rows only: the shuffles stay inside a row
@@ -136,7 +136,7 @@ __global__ void rope_table_kernel(float* cos_t, float* sin_t, int max_pos, int D
 template <int D>
 hipError_t launch_d(const RopeArgs& a, bool append, hipStream_t stream) {
   constexpr int RPB = (64 / (D / 8)) * (kThreads / 64);
-  const int64_t rows = a.num_tokens * (a.H_q + a.H_kv * (append ? 2 : 1));
+  const int64_t rows = a.num_tokens * ((a.q ? a.H_q : 0) + a.H_kv * (append ? 2 : 1));
   const int64_t blocks = (rows + RPB - 1) / RPB;
   RopeArgs args = a;
   void* kargs[] = {&args};

@@ -168,7 +168,7 @@ def time_kv_append(pcfg, k, v, dev, stream, W, traffic_key, iters=100):
                          "traffic": measured_traffic(traffic_key, "kv_append_kernel")}}
 
 
-def time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key, iters=100):
+def time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key, iters=100, with_step=True):
     """The Qwen3 step between the projections and attention on the prefill's
     B*S tokens: QK RMSNorm + NeoX RoPE in place, fused with the paged append
     of the rotated K and of V (theta 1e6, positions 0..S-1 per sequence).
@@ -214,12 +214,53 @@ def time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key, iters=100):
     nbytes = (2 * n * pcfg.H_q * row + 2 * n * pcfg.H_kv * row + n * pcfg.H_kv * row
               + 2 * n * pcfg.H_kv * row + n * D * 4 + n * 4 + n * 8)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"metric": "QK-norm + RoPE + paged append GB/s", "value": round(gbs, 1), "unit": "GB/s",
-            "tokens": n, "bytes": int(nbytes), "launch_ms": round(ms, 5),
-            "roofline": {"bound": "hbm", "kernel": "qk_norm_rope_kernel<128,append>",
-                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic(traffic_key, "qk_norm_rope_kernel")}}
+    leg = {"metric": "QK-norm + RoPE + paged append GB/s", "value": round(gbs, 1), "unit": "GB/s",
+           "tokens": n, "bytes": int(nbytes), "launch_ms": round(ms, 5),
+           "roofline": {"bound": "hbm", "kernel": "qk_norm_rope_kernel<128,append>",
+                        "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": measured_traffic(traffic_key, "qk_norm_rope_kernel")}}
+    if not with_step:
+        return leg
+    # The whole attention step of a Qwen3 prefill layer, two ways:
+    #   two-pass: norm + RoPE + append of q and k, then attn_prefill;
+    #   fused: norm + RoPE + append of k only, then attn_prefill_qk_norm_rope
+    #          (the queries are normalised and rotated as they are loaded).
+    from attention_attn_prefill_amd import attn_prefill, attn_prefill_qk_norm_rope
+    shp_q, shp_k = (pcfg.B, pcfg.S_q, pcfg.H_q, D), (pcfg.B, pcfg.S_kv, pcfg.H_kv, D)
+    q0 = torch.from_numpy(q).to(dev)
+    to = torch.empty_like(q0)
+
+    def two_pass():
+        attn_qk_norm_rope_append(tq, tk, tv, qw, kw, ct, st, pos, kc, vc, sm, stream=stream)
+        attn_prefill(tq.view(shp_q), tk.view(shp_k), tv.view(shp_k), to, causal=pcfg.causal, stream=stream)
+
+    def k_only():
+        attn_qk_norm_rope_append(None, tk, tv, None, kw, ct, st, pos, kc, vc, sm, stream=stream)
+
+    def fused():
+        k_only()
+        # positions None: query row i of each sequence is at position i
+        attn_prefill_qk_norm_rope(q0, tk.view(shp_k), tv.view(shp_k), to, qw, ct, st, None,
+                                  causal=pcfg.causal, stream=stream)
+
+    def timed(fn, reps=50):
+        for _ in range(10):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    two_ms, fused_ms, k_ms = timed(two_pass), timed(fused), timed(k_only)
+    leg["attention_step"] = {
+        "what": "QK-norm + RoPE + KV append + causal prefill on the same tokens",
+        "two_pass_us": round(two_ms * 1e3, 2), "fused_q_on_load_us": round(fused_ms * 1e3, 2),
+        "k_only_append_us": round(k_ms * 1e3, 2), "speedup": round(two_ms / fused_ms, 3)}
+    return leg
 
 
 def time_cross_module(dev, stream, W, iters=200):
@@ -478,7 +519,8 @@ def main():
         },
     }
     line["kv_append"] = time_kv_append(pcfg, k, v, dev, stream, W, traffic_key)
-    line["qk_norm_rope_append"] = time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key)
+    line["qk_norm_rope_append"] = time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key,
+                                                    with_step=not args.profile)
     line["cross_attention_module"] = time_cross_module(dev, stream, W)
     if not args.profile:
         line["shared_prefix_decode"] = time_shared_prefix(dev, stream, W)

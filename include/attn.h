@@ -265,6 +265,9 @@ attn_status_t attn_qk_norm_rope(void* q, void* k, const void* q_weight,
  * the step between the projections and attention in the pages' Qwen3 layer
  * order ("QK-norm -> RoPE -> KV append -> attn").  A token with a bad
  * position writes NaN key rows to its slot.
+ * q may be NULL (then q_weight must be NULL too): keys and values only, for
+ * a prefill that normalises and rotates Q as it loads it
+ * (attn_prefill_qk_norm_rope); k_weight alone then selects the key norm.
  */
 attn_status_t attn_qk_norm_rope_append(void* q, void* k, const void* v,
                                        const void* q_weight, const void* k_weight,
@@ -274,6 +277,35 @@ attn_status_t attn_qk_norm_rope_append(void* q, void* k, const void* v,
                                        float eps, void* k_cache, void* v_cache,
                                        const int64_t* slot_mapping, int block_size,
                                        int64_t num_blocks, void* stream);
+
+/*
+ * Causal (or not) GQA prefill with the Qwen3 QK-norm + RoPE of the queries
+ * fused into the query load ("GRPO-CUDA Project Memory" page, "RoPE design"
+ * and the Qwen3 notes): the result of attn_qk_norm_rope on q (per-head
+ * RMSNorm with q_weight, or none when NULL, then the NeoX rotation at
+ * positions[b * S_q + i], fp32, one rounding to fp16) followed by
+ * attn_prefill, without writing the rotated q anywhere (q is read only).
+ * The keys must already be normalised and rotated, e.g. by
+ * attn_qk_norm_rope_append with q = NULL, which also fills the cache.
+ *
+ *   q, k, v, o, B, S_q, S_kv, H_q, H_kv, head_dim, causal: as attn_prefill
+ *   q_weight  [head_dim] fp16 or NULL
+ *   cos_table, sin_table [max_pos, head_dim/2] fp32 (attn_rope_table)
+ *   positions [B * S_q] int32, or NULL: query row i of every sequence is at
+ *             position i (a prefill from the start of the sequence; the
+ *             table lookups then wait for nothing)
+ *
+ * Same validation and errors as attn_prefill, plus INVALID_ARG for a NULL
+ * table, max_pos <= 0, eps < 0 or a misaligned table (16 bytes), weight
+ * (16 bytes) or positions array (4 bytes).  Device-side precondition
+ * 0 <= position < max_pos; a query row that breaks it comes out NaN.
+ */
+attn_status_t attn_prefill_qk_norm_rope(const void* q, const void* k, const void* v, void* o,
+                                        const void* q_weight, const float* cos_table,
+                                        const float* sin_table, const int32_t* positions,
+                                        int B, int S_q, int S_kv, int H_q, int H_kv,
+                                        int head_dim, int max_pos, float eps, int causal,
+                                        void* stream);
 
 /*
  * Bytes of device workspace attn_cross_attention needs (the projected q, k,

@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "attn_abi_version", "attn_status_string", "attn_prefill",
+        "attn_abi_version", "attn_status_string", "attn_prefill", "attn_prefill_qk_norm_rope",
         "attn_decode_paged_workspace_size", "attn_decode_paged", "attn_kv_append",
         "attn_rope_table", "attn_qk_norm_rope", "attn_qk_norm_rope_append",
         "attn_cross_attention_workspace_size", "attn_cross_attention",
@@ -154,6 +154,27 @@ def test_rope_table_rejects(lib, kw, want):
     assert rope_table(lib, **kw) == want
 
 
+def prefill_rope(lib, q=P, k=P, v=P, o=P2, qw=P, c=P, s=P2, pos=P, B=1, S_q=64, S_kv=64, H_q=2, H_kv=1,
+                 D=128, max_pos=64, eps=1e-6, causal=1):
+    return lib.attn_prefill_qk_norm_rope(q, k, v, o, qw, c, s, pos, B, S_q, S_kv, H_q, H_kv, D, max_pos, eps,
+                                         causal, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    # the prefill's own checks come first
+    (dict(q=NULL), INV), (dict(o=NULL), INV), (dict(B=0), INV), (dict(H_q=3, H_kv=2), INV),
+    (dict(S_q=64, S_kv=65), INV), (dict(D=96), UNS), (dict(q=ctypes.c_void_p(0x10008)), INV),
+    # then the rotation's
+    (dict(c=NULL), INV), (dict(s=NULL), INV), (dict(pos=NULL, max_pos=0), INV), (dict(max_pos=0), INV),
+    (dict(eps=-1e-6), INV), (dict(eps=float("nan")), INV),
+    (dict(c=ctypes.c_void_p(0x10004)), INV), (dict(s=ctypes.c_void_p(0x20008)), INV),
+    (dict(pos=ctypes.c_void_p(0x10002)), INV), (dict(qw=ctypes.c_void_p(0x10008)), INV),
+    (dict(qw=NULL, c=NULL), INV),
+])
+def test_prefill_qk_norm_rope_rejects(lib, kw, want):
+    assert prefill_rope(lib, **kw) == want
+
+
 def qk_rope(lib, q=P, k=P2, qw=P, kw_=P2, c=P, s=P2, pos=P, n=16, H_q=16, H_kv=8, D=128,
             max_pos=64, eps=1e-6):
     return lib.attn_qk_norm_rope(q, k, qw, kw_, c, s, pos, n, H_q, H_kv, D, max_pos, eps, NULL)
@@ -174,8 +195,8 @@ def test_qk_norm_rope_rejects(lib, kw, want):
     assert qk_rope(lib, **kw) == want
 
 
-def qk_rope_append(lib, v=P, kc=P2, vc=P2, sm=P, bs=16, nb=4, n=16, D=128):
-    return lib.attn_qk_norm_rope_append(P, P2, v, P, P2, P, P2, P, n, 16, 8, D, 64, 1e-6, kc, vc, sm,
+def qk_rope_append(lib, q=P, qw=P, kw_=P2, v=P, kc=P2, vc=P2, sm=P, bs=16, nb=4, n=16, D=128):
+    return lib.attn_qk_norm_rope_append(q, P2, v, qw, kw_, P, P2, P, n, 16, 8, D, 64, 1e-6, kc, vc, sm,
                                         bs, nb, NULL)
 
 
@@ -184,6 +205,9 @@ def qk_rope_append(lib, v=P, kc=P2, vc=P2, sm=P, bs=16, nb=4, n=16, D=128):
     (dict(bs=0), INV), (dict(nb=0), INV), (dict(D=64 + 8), UNS),
     (dict(sm=ctypes.c_void_p(0x10004)), INV), (dict(v=ctypes.c_void_p(0x10008)), INV),
     (dict(n=0), OK),
+    # keys and values only (q NULL): q_weight must be NULL too
+    (dict(q=NULL), INV), (dict(q=NULL, kw_=NULL), INV), (dict(q=NULL, qw=NULL, v=NULL), INV),
+    (dict(q=NULL, qw=NULL, kw_=ctypes.c_void_p(0x20008)), INV), (dict(q=NULL, qw=NULL, n=0), OK),
 ])
 def test_qk_norm_rope_append_rejects(lib, kw, want):
     assert qk_rope_append(lib, **kw) == want

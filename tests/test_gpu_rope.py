@@ -198,3 +198,109 @@ def test_end_to_end_norm_rope_then_causal_prefill():
     rq = ora_qk(q.reshape(B * S, H_q, D), qw, pos, 4096, theta).astype(np.float16).reshape(q.shape)
     rk = ora_qk(k.reshape(B * S, H_kv, D), kw, pos, 4096, theta).astype(np.float16).reshape(k.shape)
     assert_parity(host(to), oracle.prefill(rq, rk, v, causal=True), "prefill after rope")
+
+
+def gpu_prefill_q_rope(q, k_rot, v, qw, pos, max_pos, theta, causal, eps=1e-6):
+    """attn_prefill_qk_norm_rope on unrotated q and already rotated k."""
+    import torch
+    from attention_attn_prefill_amd import attn_prefill_qk_norm_rope
+    c, s = gpu_tables(max_pos, q.shape[-1], theta)
+    tq = dev(q)
+    to = torch.empty_like(tq)
+    attn_prefill_qk_norm_rope(tq, dev(k_rot), dev(v), to, None if qw is None else dev(qw), c, s,
+                              dev(np.asarray(pos, np.int32)), eps=eps, causal=causal)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(tq).view(np.uint16), q.view(np.uint16)), "q must be read only"
+    return host(to)
+
+
+PREFILL_ROPE_CASES = [  # B, S_q, S_kv, H_q, H_kv, D, causal, norm, theta
+    (2, 300, 300, 16, 8, 128, True, True, 1e6),    # two heads per workgroup, ragged tail
+    (1, 200, 200, 3, 1, 128, True, False, 1e4),    # one head per workgroup, rotation only
+    (2, 77, 150, 4, 2, 64, False, True, 1e4),      # non-causal, S_q != S_kv
+    (3, 64, 96, 8, 8, 32, False, True, 5e5),       # D = 32
+]
+
+
+@pytest.mark.parametrize("B,S_q,S_kv,H_q,H_kv,D,causal,norm,theta", PREFILL_ROPE_CASES)
+def test_prefill_with_q_norm_rope_on_load(B, S_q, S_kv, H_q, H_kv, D, causal, norm, theta):
+    """GPU: keys through the K-only fused append (q = None), then prefill with
+    the query norm + rotation on load.  Against the oracle (norm + rotation in
+    fp64, rounded to fp16, then attention) at the attention tolerance, and
+    against the two-pass GPU path (attn_qk_norm_rope, then attn_prefill)."""
+    import torch
+    from attention_attn_prefill_amd import attn_prefill, attn_qk_norm_rope, attn_qk_norm_rope_append
+    max_pos = 4096
+    q, k, v = _rand((B, S_q, H_q, D), 51 + D), _rand((B, S_kv, H_kv, D), 52 + D), _rand((B, S_kv, H_kv, D), 53)
+    qw, kw = (_weight(D, 54), _weight(D, 55)) if norm else (None, None)
+    rng = np.random.default_rng(S_q + S_kv)
+    qpos = rng.integers(0, max_pos, B * S_q).astype(np.int32)
+    kpos = rng.integers(0, max_pos, B * S_kv).astype(np.int32)
+    say("prefill with q rope on load", B, S_q, S_kv, H_q, H_kv, D, causal, norm)
+    # keys: K-only fused append into a cache of B*S_kv slots
+    nb = (B * S_kv + 15) // 16
+    c, s = gpu_tables(max_pos, D, theta)
+    tk = dev(k)
+    kc = torch.zeros((nb, H_kv, 16, D), dtype=torch.float16, device="cuda")
+    vc = torch.zeros_like(kc)
+    slots = dev(np.arange(B * S_kv, dtype=np.int64))
+    attn_qk_norm_rope_append(None, tk, dev(v), None, None if kw is None else dev(kw), c, s, dev(kpos), kc, vc,
+                             slots)
+    torch.cuda.synchronize()
+    k_rot = host(tk)
+    ref_k = ora_qk(k.reshape(-1, H_kv, D), kw, kpos, max_pos, theta)
+    assert_rope_parity(k_rot.reshape(-1, H_kv, D), ref_k, "k (K-only append)")
+    kflat = host(kc).transpose(0, 2, 1, 3).reshape(nb * 16, H_kv, D)[:B * S_kv]
+    assert np.array_equal(kflat.view(np.uint16), k_rot.reshape(-1, H_kv, D).view(np.uint16))
+    got = gpu_prefill_q_rope(q, k_rot, v, qw, qpos, max_pos, theta, causal)
+    rq = ora_qk(q.reshape(-1, H_q, D), qw, qpos, max_pos, theta).astype(np.float16).reshape(q.shape)
+    assert_parity(got, oracle.prefill(rq, k_rot, v, causal=causal), "prefill, q rotated on load")
+    # the two-pass path on the GPU: q rotated in place by attn_qk_norm_rope
+    # (with a throw-away k of q's token count), then attn_prefill
+    tq = dev(q)
+    dummy_k = torch.zeros((B * S_q, H_kv, D), dtype=torch.float16, device="cuda")
+    attn_qk_norm_rope(tq, dummy_k, None if qw is None else dev(qw), None if kw is None else dev(kw), c, s,
+                      dev(qpos))
+    to = torch.empty_like(tq)
+    attn_prefill(tq, dev(k_rot), dev(v), to, causal=causal)
+    torch.cuda.synchronize()
+    # the rotated queries can differ in rare elements by one fp16 rounding
+    # (the norm sums squares in another order; the separate pass rounds its
+    # last fma straight to fp16), so the two outputs agree to the attention
+    # tolerance, and each matches the oracle
+    assert_parity(got, host(to).astype(np.float64), "on-load vs two-pass")
+
+
+def test_prefill_q_rope_bad_positions_give_nan_rows():
+    """Query rows whose position has no table row come out NaN; the other
+    rows are unaffected."""
+    B, S, H_q, H_kv, D, max_pos = 1, 130, 4, 2, 128, 512
+    q, k, v = _rand((B, S, H_q, D), 61), _rand((B, S, H_kv, D), 62), _rand((B, S, H_kv, D), 63)
+    pos = np.arange(S, dtype=np.int32)
+    pos[[3, 64, 129]] = [-1, max_pos, 1 << 30]
+    say("prefill q rope, bad positions")
+    got = gpu_prefill_q_rope(q, k, v, _weight(D, 64), pos, max_pos, 1e6, True)
+    bad = np.zeros(S, bool)
+    bad[[3, 64, 129]] = True
+    assert np.isnan(got[0, bad].astype(np.float64)).all()
+    rq = ora_qk(q.reshape(-1, H_q, D), _weight(D, 64), np.where(bad, 0, pos), max_pos, 1e6)
+    rq = rq.astype(np.float16).reshape(q.shape)
+    ref = oracle.prefill(rq, k, v, causal=True)
+    assert_parity(got[0, ~bad], ref[0, ~bad], "rows with valid positions")
+
+
+def test_prefill_q_rope_null_positions_are_row_indices():
+    """positions = None means query row i of every sequence is at position
+    i: the same output, bit for bit, as passing 0..S-1 per sequence."""
+    B, S, H_q, H_kv, D, max_pos = 2, 200, 8, 4, 128, 1024
+    q, k, v = _rand((B, S, H_q, D), 71), _rand((B, S, H_kv, D), 72), _rand((B, S, H_kv, D), 73)
+    qw = _weight(D, 74)
+    say("prefill q rope, positions None")
+    explicit = gpu_prefill_q_rope(q, k, v, qw, np.tile(np.arange(S, dtype=np.int32), B), max_pos, 1e6, True)
+    import torch
+    from attention_attn_prefill_amd import attn_prefill_qk_norm_rope
+    c, s = gpu_tables(max_pos, D, 1e6)
+    to = torch.empty((B, S, H_q, D), dtype=torch.float16, device="cuda")
+    attn_prefill_qk_norm_rope(dev(q), dev(k), dev(v), to, dev(qw), c, s, None, causal=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(to).view(np.uint16), explicit.view(np.uint16))
