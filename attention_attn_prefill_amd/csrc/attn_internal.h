@@ -124,7 +124,7 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_pos, int head_d
 constexpr int kDecodeBlockSize = 16;
 constexpr int kDecodeHeadDim = 128;
 int decode_split_blocks(int num_seqs, int H_kv, int max_blocks_per_seq);
-constexpr int kPrefixChunkBlocks = 32;  // prefix blocks per prefix-kernel workgroup
+constexpr int kPrefixChunkBlocks = 64;  // prefix blocks per prefix-kernel workgroup
 constexpr int kDecodeSingleSplitPairs = 2048;  // shared-prefix decode: one split per sequence from here
 
 // Shared-prefix mode: the group gi of sequence s (group_start ascending,

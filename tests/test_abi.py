@@ -257,13 +257,13 @@ def test_shared_prefix_rejects(lib, kw, want):
 
 def test_shared_prefix_workspace_size(lib):
     # 256 seqs x 8 kv heads = 2048 pairs: one split per sequence, so
-    # 256 x 16 heads x (prefix slots ceil(160/32) = 5 + 1 split) x 130 floats,
+    # 256 x 16 heads x (prefix slots ceil(160/64) = 3 + 1 split) x 130 floats,
     # then one int32 prefix length per sequence
     n = lib.attn_decode_paged_shared_prefix_workspace_size(256, 16, 8, 128, 160, 16, 32, 8)
-    assert n == 256 * 16 * (5 + 1) * 130 * 4 + 256 * 4
+    assert n == 256 * 16 * (3 + 1) * 130 * 4 + 256 * 4
     # 64 x 8 = 512 pairs: the plain split rule (largest of 128/64/32/16 blocks
     # giving >= 2048 workgroups): 32 blocks, ceil(160/32) = 5 splits
     n = lib.attn_decode_paged_shared_prefix_workspace_size(64, 16, 8, 128, 160, 16, 8, 8)
-    assert n == 64 * 16 * (5 + 5) * 130 * 4 + 64 * 4
+    assert n == 64 * 16 * (3 + 5) * 130 * 4 + 64 * 4
     assert lib.attn_decode_paged_shared_prefix_workspace_size(256, 16, 8, 128, 160, 16, 0, 8) == 0
     assert lib.attn_decode_paged_shared_prefix_workspace_size(256, 16, 8, 64, 160, 16, 32, 8) == 0
