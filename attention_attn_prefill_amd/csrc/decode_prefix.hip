@@ -70,7 +70,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 // early-clobber: a read's destination must not be the address register
 // that a later read of the block still uses (its data can land before the
 // later read issues).
-__device__ __forceinline__ void lds_read_tr_tile(const uint32_t (&addr)[1], short4_t (&r)[1][4]) {
+[[maybe_unused]] __device__ __forceinline__ void lds_read_tr_tile(const uint32_t (&addr)[1], short4_t (&r)[1][4]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %4\n\t"
       "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
@@ -84,7 +84,7 @@ __device__ __forceinline__ void lds_read_tr_tile(const uint32_t (&addr)[1], shor
 
 // The same for four head-dim slices (a wavefront that owns all of O):
 // sixteen reads, one wait.
-__device__ __forceinline__ void lds_read_tr_tile(const uint32_t (&addr)[4], short4_t (&r)[4][4]) {
+[[maybe_unused]] __device__ __forceinline__ void lds_read_tr_tile(const uint32_t (&addr)[4], short4_t (&r)[4][4]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %16\n\t"
       "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
