@@ -49,6 +49,8 @@ CASES = [  # B, T_q, T_k, dim, H, base
     (1, 33, 100, 128, 1, 5e5),    # D = 128
     (3, 64, 64, 256, 4, 1e4),     # D = 64
     (2, 200, 77, 96, 3, 1e6),     # dim 96: three column tiles, ragged rows
+    (1, 40, 33, 1024, 8, 1e4),    # wide: 32 column tiles, D = 128
+    (1, 33, 20, 2048, 16, 1e4),   # wider still: K = 2048, many k-steps per wavefront
 ]
 
 
