@@ -34,6 +34,10 @@
 //     in real arithmetic (any reference point cancels in O/l); the weights stay
 //     below 2^8, far inside fp16 range.  The row sum l adds up the fp16 weights
 //     that actually enter the PV product (v_dot2_f32_f16 against ones);
+//   * with two heads per workgroup the wavefronts of the two heads that share
+//     a SIMD run each step in opposite order (MFMA phase then softmax, and
+//     softmax then MFMA phase), at raised issue priority during their MFMA
+//     phase, so one wavefront's exponentials overlap the other's matrix work;
 //   * causal: tiles strictly above the diagonal are never loaded; only tiles
 //     crossing the diagonal (or the ragged end) are masked element-wise;
 //   * a workgroup runs query tiles i and n-1-i back to back: under the causal
@@ -290,6 +294,26 @@ struct QNormRope {
   }
 };
 
+// Issue order of a GEMM phase: kLdsAhead operand reads first, then each
+// MFMA followed by up to two more reads, so the LDS reads of later operands
+// are in flight while earlier MFMAs run (the scheduler otherwise keeps only
+// one or two reads ahead and each MFMA group waits out a full LDS latency).
+constexpr int kLdsAhead = 8;
+
+template <int I, int NM, int REM>
+struct IssueChain {
+  static __device__ __forceinline__ void run() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int k = REM < 2 ? REM : 2;
+    if constexpr (k > 0) __builtin_amdgcn_sched_group_barrier(0x100, k, 0);  // LDS reads
+    IssueChain<I + 1, NM, REM - k>::run();
+  }
+};
+template <int NM, int REM>
+struct IssueChain<NM, NM, REM> {
+  static __device__ __forceinline__ void run() {}
+};
+
 // All per-wavefront state of one prefill workgroup, and the per-tile step.
 template <int D, bool CAUSAL, int HP>
 struct Prefill {
@@ -319,6 +343,10 @@ struct Prefill {
     if (t + 1 < n_tiles) st.load_v((t + 1) * kBlockN, tid);
   }
   __device__ __forceinline__ void commit_loads(int t) {
+    // K(t+2) goes into the slot that held K(t); K(0) is read by the QK
+    // product that precedes the loop, so before the first store every
+    // wavefront must be past that read
+    if (t == 0) __syncthreads();
     if (t + 2 < n_tiles) st.store_k(k_lds + (t & 1) * K_LDS, tid);
     if (t + 1 < n_tiles) st.store_v(vt_lds + ((t + 1) & 1) * V_LDS, tid);
     __syncthreads();
@@ -398,6 +426,84 @@ struct Prefill {
       }
     }
     commit_loads(t);
+  }
+
+  // ---- the two phases of the ping-pong schedule (HP == 2) ----
+  half8_t pf[4];  // fp16 weights of the tile whose PV product is next
+
+  // VALU phase: mask, tile max, lazy rescale and the exponentials of tile
+  // t's scores sc -> pf, with the row sum of the fp16 weights
+  __device__ __forceinline__ void softmax(int t, f32x16_t (&sc)[2]) {
+    const int kv0 = t * kBlockN;
+    const bool need_mask = (CAUSAL && kv0 + kBlockN - 1 > qw) || (kv0 + kBlockN > S_kv);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+          const bool masked = (CAUSAL && key > qrow) || key >= S_kv;
+          if (masked) sc[kb][r] = -INFINITY;
+        }
+      }
+    }
+    float mx = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[0][r], sc[0][r + 1]));
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[1][r], sc[1][r + 1]));
+    mx = wave_half_swap_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m + lazy_raw) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - m_new) * c2);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    const float mb = m * c2;
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four independent partial sums
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pf[c][i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[c >> 1][8 * (c & 1) + i], c2, -mb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t pp = {pf[c][2 * i], pf[c][2 * i + 1]};
+        lp[i] = __builtin_amdgcn_fdot2(pp, ones, lp[i], false);
+      }
+    }
+    l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+  }
+
+  // MFMA phase: the scores of tile t+1 into sn (when QK), then O += P(t) V(t).
+  // The wavefront raises its issue priority for the phase, so on a SIMD the
+  // MFMAs of this wavefront go first and the other's VALU fills the gaps.
+  template <bool QK>
+  __device__ __forceinline__ void gemm(int t, f32x16_t (&sn)[2]) {
+    __builtin_amdgcn_s_setprio(1);
+    if (QK) qk(sn, t + 1);
+    const _Float16* vl = vt_lds + (t & 1) * V_LDS + v_lane;
+    constexpr int N = DT * 4;
+    constexpr int R = 4;
+    half8_t ring[R];
+#pragma unroll
+    for (int n = 0; n < R; ++n) ring[n] = pv_operand<VROW>(vl, n % DT, n / DT);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int dt = n % DT, c = n / DT;
+      const half8_t vf = ring[n % R];
+      if (n + R < N) ring[n % R] = pv_operand<VROW>(vl, (n + R) % DT, (n + R) / DT);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], o[dt], 0, 0, 0);
+    }
+    // QK: 2*(D/16) MFMAs, one b128 read each; PV: 4*DT MFMAs, two reads each
+    constexpr int NM = (QK ? 2 * KS : 0) + 4 * DT;
+    constexpr int NR = (QK ? 2 * KS : 0) + 8 * DT;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
+    IssueChain<0, NM, NR - kLdsAhead>::run();
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // a tile this wavefront does not compute (above its diagonal): staging only
@@ -489,8 +595,41 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
   __syncthreads();
 
   // Every wavefront takes part in all n_tiles staging steps (and barriers);
-  // it computes tiles [0, wave_tiles).  Pairs of steps swap the two score
-  // buffers so no copy is needed.
+  // it computes tiles [0, wave_tiles).
+  if constexpr (HP == 2) {
+    // Ping-pong: SIMD s runs wavefront s (first head) and s + 4 (second head)
+    // on the same rows.  Per step the first runs its MFMA phase, then its
+    // softmax; the second its softmax, then its MFMA phase.  Each SIMD so
+    // pairs one wavefront's MFMAs with the other's VALU work instead of both
+    // doing the same kind of work at once.
+    //   first head,  step t: QK(t+1), PV(t) | softmax(t+1)
+    //   second head, step t: softmax(t)     | QK(t+1), PV(t)
+    f32x16_t sc[2];
+    const bool first = wave < kWavesPerHead;
+    if (wave_tiles > 0) {
+      p.qk(sc, 0);
+      if (first) p.softmax(0, sc);
+    }
+    int t = 0;
+    for (; t < wave_tiles; ++t) {
+      p.issue_loads(t);
+      const bool more = t + 1 < wave_tiles;
+      if (first) {
+        if (more) p.template gemm<true>(t, sc); else p.template gemm<false>(t, sc);
+        __builtin_amdgcn_sched_barrier(0);  // keep the phases apart
+        if (more) p.softmax(t + 1, sc);
+      } else {
+        p.softmax(t, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) p.template gemm<true>(t, sc); else p.template gemm<false>(t, sc);
+      }
+      p.commit_loads(t);
+    }
+    for (; t < n_tiles; ++t) p.idle_step(t);
+  } else {
+  // One head per workgroup: the scores of tile t+1 are computed inside step t,
+  // among tile t's exponentials.  Pairs of steps swap the two score buffers so
+  // no copy is needed.
   f32x16_t sa[2], sb[2];
   if (wave_tiles > 0) p.qk(sa, 0);
   int t = 0;
@@ -507,6 +646,7 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
     t += 1;
   }
   for (; t < n_tiles; ++t) p.idle_step(t);
+  }
 
   // epilogue: combine the two half-row sums, normalise, round to fp16
   if (p.qw >= a.S_q) return;
