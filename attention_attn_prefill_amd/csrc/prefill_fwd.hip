@@ -89,6 +89,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const _Float16* p, i
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// Workgroup barrier that orders LDS accesses only.  The wavefronts of a
+// workgroup exchange data through LDS alone, so the barrier need not wait for
+// outstanding global loads or stores (__syncthreads() does: its workgroup
+// fence covers global memory too, and a query tile's output stores or the
+// next tiles' loads would then be waited out at every barrier).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Row stride (halfs) of the V tile in LDS.  The PV operand is read with
 // ds_read_b64_tr_b16, where the 16 lanes of a group read 4 key rows x 16
 // dims; a stride of 16 dwords modulo the 64 banks keeps those rows on
@@ -127,13 +138,14 @@ struct Stager {
   }
   __device__ __forceinline__ static bool mine(int u, int tid) { return tid + u * kThreads < VECS; }
 
-  __device__ __forceinline__ void load_k(int kv0, int tid) {
+  __device__ __forceinline__ void load_k(int kv0, int tid) { load_k_into(kreg, kv0, tid); }
+  __device__ __forceinline__ void load_k_into(half8_t (&dst)[PER_T], int kv0, int tid) const {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       if (!mine(u, tid)) continue;
       const int idx = tid + u * kThreads;
       const int r = idx / VEC_PER_ROW, c = idx % VEC_PER_ROW;
-      kreg[u] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(krsrc, (kv0 + r) * row_bytes + 16 * c, 0, 0));
+      dst[u] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(krsrc, (kv0 + r) * row_bytes + 16 * c, 0, 0));
     }
   }
   __device__ __forceinline__ void load_v(int kv0, int tid) {
@@ -145,13 +157,14 @@ struct Stager {
       vreg[u] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (kv0 + r) * row_bytes + 16 * c, 0, 0));
     }
   }
-  __device__ __forceinline__ void store_k(_Float16* k_lds, int tid) const {
+  __device__ __forceinline__ void store_k(_Float16* k_lds, int tid) const { store_k_from(kreg, k_lds, tid); }
+  __device__ __forceinline__ static void store_k_from(const half8_t (&src)[PER_T], _Float16* k_lds, int tid) {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       if (!mine(u, tid)) continue;
       const int idx = tid + u * kThreads;
       const int r = idx / VEC_PER_ROW, c = idx % VEC_PER_ROW;
-      *reinterpret_cast<half8_t*>(&k_lds[r * KROW + 8 * c]) = kreg[u];
+      *reinterpret_cast<half8_t*>(&k_lds[r * KROW + 8 * c]) = src[u];
     }
   }
   __device__ __forceinline__ void store_v(_Float16* v_lds, int tid) const {
@@ -346,10 +359,10 @@ struct Prefill {
     // K(t+2) goes into the slot that held K(t); K(0) is read by the QK
     // product that precedes the loop, so before the first store every
     // wavefront must be past that read
-    if (t == 0) __syncthreads();
+    if (t == 0) lds_barrier();
     if (t + 2 < n_tiles) st.store_k(k_lds + (t & 1) * K_LDS, tid);
     if (t + 1 < n_tiles) st.store_v(vt_lds + ((t + 1) & 1) * V_LDS, tid);
-    __syncthreads();
+    lds_barrier();
   }
 
   __device__ __forceinline__ void qk(f32x16_t (&s)[2], int t) const {
@@ -582,17 +595,17 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
   if constexpr (ROPE) {
     if (a.positions) qr.tables(a, p.hf);  // as soon as the position is in
   }
+  // K(0), V(0) and K(1) in flight together: one global round trip
+  half8_t k1[Stager<D, HP>::PER_T];
   p.st.load_k(0, p.tid);
   p.st.load_v(0, p.tid);
+  if (n_tiles > 1) p.st.load_k_into(k1, kBlockN, p.tid);
   bool q_ok = true;
   if constexpr (ROPE) q_ok = qr.apply(a, p.qf);
   p.st.store_k(k_lds, p.tid);
   p.st.store_v(vt_lds, p.tid);
-  if (n_tiles > 1) {
-    p.st.load_k(kBlockN, p.tid);
-    p.st.store_k(k_lds + P::K_LDS, p.tid);
-  }
-  __syncthreads();
+  if (n_tiles > 1) Stager<D, HP>::store_k_from(k1, k_lds + P::K_LDS, p.tid);
+  lds_barrier();
 
   // Every wavefront takes part in all n_tiles staging steps (and barriers);
   // it computes tiles [0, wave_tiles).
@@ -691,7 +704,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, 2) void prefill_fwd_kernel
   const int lo = pair, hi = a.n_qtiles - 1 - pair;
   prefill_qtile<D, CAUSAL, HP, ROPE>(a, hi, hg, b, k_lds, vt_lds);
   if (lo < hi) {
-    __syncthreads();  // the first tile's last LDS reads are done
+    lds_barrier();  // the first tile's last LDS reads are done (its output stores may still be in flight)
     prefill_qtile<D, CAUSAL, HP, ROPE>(a, lo, hg, b, k_lds, vt_lds);
   }
 }
