@@ -68,6 +68,11 @@ EDGE = [
     (1, 130, 7, 2, 2, 64, False),
     (1, 256, 64, 8, 8, 32, False),
     (1, 384, 384, 2, 1, 128, False),
+    # several query-tile pairs with a ragged last tile, and an odd middle
+    # tile, on two-head workgroups (each SIMD pairs the two heads' wavefronts)
+    (2, 1000, 1000, 4, 2, 128, True),
+    (1, 777, 777, 8, 2, 128, True),
+    (1, 520, 520, 4, 2, 128, False),
 ]
 
 
