@@ -661,12 +661,22 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
   for (; t < n_tiles; ++t) p.idle_step(t);
   }
 
-  // epilogue: combine the two half-row sums, normalise, round to fp16
+  // epilogue: combine the two half-row sums, normalise, round to fp16.
+  // A lane holds 4-dim pieces of one row, so storing them directly would
+  // scatter 8-byte writes over 32 rows per instruction.  Instead each
+  // wavefront puts its 32 x D tile row-major into its own part of the K/V
+  // tiles' LDS (free: every wavefront is past the last step's barrier, and
+  // the next query tile writes it only after the workgroup barrier that
+  // follows), reads it back as 16-byte row pieces and stores whole rows.
   if (p.qw >= a.S_q) return;
   const float lsum = wave_half_swap_add(p.l);
-  if (p.qrow >= a.S_q) return;
   const float inv = 1.0f / lsum;
-  _Float16* op = a.o + ((int64_t)b * a.S_q + p.qrow) * q_row_stride + (int64_t)h * D;
+  // row stride (halfs): a multiple of 8 for the 16-byte reads; with it the
+  // 4 tiles of a head fit the V tiles (first head) and the K tiles (second)
+  constexpr int OROW = (D == 32) ? D : D + 8;
+  static_assert(4 * kRowsPerWave * OROW <= 2 * P::V_LDS && 4 * kRowsPerWave * OROW <= 2 * P::K_LDS,
+                "output tiles must fit the K/V tiles' LDS");
+  _Float16* ot = (wave < kWavesPerHead ? vt_lds : k_lds) + (wave % kWavesPerHead) * kRowsPerWave * OROW;
 #pragma unroll
   for (int dt = 0; dt < P::DT; ++dt) {
 #pragma unroll
@@ -675,8 +685,21 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[j] = (_Float16)(p.o[dt][rg * 4 + j] * inv);
       if (ROPE && !q_ok) out = __builtin_bit_cast(half4_t, 0x7e007e007e007e00ull);  // quiet NaN bits
-      *reinterpret_cast<half4_t*>(op + dt * 32 + rg * 8 + p.hf * 4) = out;
+      *reinterpret_cast<half4_t*>(ot + col * OROW + dt * 32 + rg * 8 + p.hf * 4) = out;
     }
+  }
+  // the lanes read rows other lanes of this wavefront wrote
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  constexpr int PIECES = D / 8;             // 16-byte pieces per row
+  constexpr int ROWS_PER = 64 / PIECES;     // rows per 64-lane store
+  const int pr = lane / PIECES, pc = lane % PIECES;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / ROWS_PER; ++i) {
+    const int r = i * ROWS_PER + pr;
+    const half8_t v8 = *reinterpret_cast<const half8_t*>(ot + r * OROW + 8 * pc);
+    if (p.qw + r < a.S_q)
+      *reinterpret_cast<half8_t*>(a.o + ((int64_t)b * a.S_q + p.qw + r) * q_row_stride + (int64_t)h * D + 8 * pc) = v8;
   }
 }
 
