@@ -369,84 +369,12 @@ struct Prefill {
     qk_tile<D>(s, k_lds + (t & 1) * K_LDS + k_lane, qf);
   }
 
-  // Softmax of tile t's scores and its PV product; when NEXT, the scores of
-  // tile t+1 are computed in the same basic block so that the scheduler can
-  // interleave those MFMAs with this tile's exponentials.
-  template <bool NEXT>
-  __device__ __forceinline__ void step(int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
-    issue_loads(t);
-    const int kv0 = t * kBlockN;
-    // element-wise mask only where the tile crosses the diagonal or the end
-    const bool need_mask = (CAUSAL && kv0 + kBlockN - 1 > qw) || (kv0 + kBlockN > S_kv);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-          const bool masked = (CAUSAL && key > qrow) || key >= S_kv;
-          if (masked) sc[kb][r] = -INFINITY;
-        }
-      }
-    }
-    // tile max of this query over both lane halves
-    float mx = fmaxf(sc[0][0], sc[0][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[0][r], sc[0][r + 1]));
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[1][r], sc[1][r + 1]));
-    mx = wave_half_swap_max(mx);
-    // move the reference point only when some row's weights would pass 2^8
-    if (__builtin_amdgcn_ballot_w64(mx > m + lazy_raw) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - m_new) * c2);
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-    const float mb = m * c2;
-    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-
-    if (NEXT) qk(sn, t + 1);
-
-    half8_t pf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pf[c][i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[c >> 1][8 * (c & 1) + i], c2, -mb));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half2_t pp = {pf[c][2 * i], pf[c][2 * i + 1]};
-        l = __builtin_amdgcn_fdot2(pp, ones, l, false);
-      }
-    }
-    // O^T += V^T P^T, the DT accumulators alternating, reads four ahead
-    const _Float16* vl = vt_lds + (t & 1) * V_LDS + v_lane;
-    {
-      constexpr int N = DT * 4;
-      constexpr int R = 4;
-      half8_t ring[R];
-#pragma unroll
-      for (int n = 0; n < R; ++n) ring[n] = pv_operand<VROW>(vl, n % DT, n / DT);
-#pragma unroll
-      for (int n = 0; n < N; ++n) {
-        const int dt = n % DT, c = n / DT;
-        const half8_t vf = ring[n % R];
-        if (n + R < N) ring[n % R] = pv_operand<VROW>(vl, (n + R) % DT, (n + R) / DT);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], o[dt], 0, 0, 0);
-      }
-    }
-    commit_loads(t);
-  }
-
-  // ---- the two phases of the ping-pong schedule (HP == 2) ----
   half8_t pf[4];  // fp16 weights of the tile whose PV product is next
 
-  // VALU phase: mask, tile max, lazy rescale and the exponentials of tile
-  // t's scores sc -> pf, with the row sum of the fp16 weights
-  __device__ __forceinline__ void softmax(int t, f32x16_t (&sc)[2]) {
+  // Mask (only where the tile crosses the diagonal or the end of the keys),
+  // tile max of each query over both lane halves, and the lazy move of the
+  // reference point: only when some row's weights would pass 2^8.
+  __device__ __forceinline__ void mask_max_rescale(int t, f32x16_t (&sc)[2]) {
     const int kv0 = t * kBlockN;
     const bool need_mask = (CAUSAL && kv0 + kBlockN - 1 > qw) || (kv0 + kBlockN > S_kv);
     if (need_mask) {
@@ -474,9 +402,14 @@ struct Prefill {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
+  }
+
+  // fp16 weights exp2(s*c2 - m*c2) -> pf, and the row sum of exactly those
+  // fp16 values (four independent partial sums)
+  __device__ __forceinline__ void weights(const f32x16_t (&sc)[2]) {
     const float mb = m * c2;
     const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four independent partial sums
+    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -491,13 +424,9 @@ struct Prefill {
     l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
   }
 
-  // MFMA phase: the scores of tile t+1 into sn (when QK), then O += P(t) V(t).
-  // The wavefront raises its issue priority for the phase, so on a SIMD the
-  // MFMAs of this wavefront go first and the other's VALU fills the gaps.
-  template <bool QK>
-  __device__ __forceinline__ void gemm(int t, f32x16_t (&sn)[2]) {
-    __builtin_amdgcn_s_setprio(1);
-    if (QK) qk(sn, t + 1);
+  // O^T += V^T P^T for tile t, the DT accumulators alternating, operand
+  // reads four ahead
+  __device__ __forceinline__ void pv(int t) {
     const _Float16* vl = vt_lds + (t & 1) * V_LDS + v_lane;
     constexpr int N = DT * 4;
     constexpr int R = 4;
@@ -511,6 +440,38 @@ struct Prefill {
       if (n + R < N) ring[n % R] = pv_operand<VROW>(vl, (n + R) % DT, (n + R) / DT);
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], o[dt], 0, 0, 0);
     }
+  }
+
+  // One step of the one-head schedule: softmax of tile t's scores and its PV
+  // product; when NEXT, the scores of tile t+1 are computed in the same basic
+  // block so that the scheduler can interleave those MFMAs with this tile's
+  // exponentials.
+  template <bool NEXT>
+  __device__ __forceinline__ void step(int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    issue_loads(t);
+    mask_max_rescale(t, sc);
+    if (NEXT) qk(sn, t + 1);
+    weights(sc);
+    pv(t);
+    commit_loads(t);
+  }
+
+  // ---- the two phases of the ping-pong schedule (HP == 2) ----
+
+  // VALU phase: tile t's scores sc -> fp16 weights pf
+  __device__ __forceinline__ void softmax(int t, f32x16_t (&sc)[2]) {
+    mask_max_rescale(t, sc);
+    weights(sc);
+  }
+
+  // MFMA phase: the scores of tile t+1 into sn (when QK), then O += P(t) V(t).
+  // The wavefront raises its issue priority for the phase, so on a SIMD the
+  // MFMAs of this wavefront go first and the other's VALU fills the gaps.
+  template <bool QK>
+  __device__ __forceinline__ void gemm(int t, f32x16_t (&sn)[2]) {
+    __builtin_amdgcn_s_setprio(1);
+    if (QK) qk(sn, t + 1);
+    pv(t);
     // QK: 2*(D/16) MFMAs, one b128 read each; PV: 4*DT MFMAs, two reads each
     constexpr int NM = (QK ? 2 * KS : 0) + 4 * DT;
     constexpr int NR = (QK ? 2 * KS : 0) + 8 * DT;
