@@ -73,6 +73,9 @@ EDGE = [
     (2, 1000, 1000, 4, 2, 128, True),
     (1, 777, 777, 8, 2, 128, True),
     (1, 520, 520, 4, 2, 128, False),
+    # non-causal, S_q != S_kv, two-head workgroups at D = 32 and 64
+    (2, 200, 150, 4, 2, 32, False),
+    (1, 300, 260, 8, 2, 64, False),
 ]
 
 
