@@ -26,6 +26,7 @@ FLAGS = [
 # lowers to v_max3_f32 without canonicalising every MFMA result first.
 PER_FILE_FLAGS = {
     "prefill_fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+    "prefill_dual.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
 }
 
 

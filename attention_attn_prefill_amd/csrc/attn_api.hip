@@ -80,8 +80,10 @@ static attn_status_t prefill_args(const void* q, const void* k, const void* v, v
     return ATTN_ERR_INVALID_ARG;
   // one workgroup per (128 query rows, q head, batch) must fit a 1-D grid
   if (ceil_div64(S_q, 128) * H_q * B > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
-  // K/V rows of one batch entry are addressed with 32-bit byte offsets
-  if ((int64_t)S_kv * H_kv * head_dim * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  // K/V rows of one batch entry are addressed with 32-bit byte offsets; the
+  // kernels address whole 64-key tiles and stage up to three tiles past the
+  // last one (those loads fall outside the buffer range and read zero)
+  if ((ceil_div64(S_kv, 64) + 3) * 64 * H_kv * head_dim * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
 
   a.q = static_cast<const _Float16*>(q);
   a.k = static_cast<const _Float16*>(k);

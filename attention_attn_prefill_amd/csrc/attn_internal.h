@@ -113,6 +113,8 @@ struct ProjArgs {
 
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool causal, hipStream_t stream);
+// head_dim 128 without the fused Q rotation: two row blocks per wavefront
+hipError_t launch_prefill_dual(const PrefillArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_qk_norm_rope(const RopeArgs& a, int head_dim, bool append, hipStream_t stream);

@@ -1,0 +1,89 @@
+// gfx950_device.h -- small device helpers shared by the prefill kernels of
+// libattn.so (cross-lane swaps, buffer resources, LDS-only barriers and the
+// transposing LDS read).  Not installed; not part of the ABI.
+#pragma once
+
+#include "attn_internal.h"
+
+namespace attn {
+namespace dev {
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// max / sum of x over lanes l and l ^ 32 (both halves end with the same value)
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_add(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A raw buffer resource over [p, p + bytes).  The base address goes through
+// readfirstlane so the descriptor lives in SGPRs (it is workgroup-uniform; a
+// VGPR descriptor would turn every load into a waterfall loop).  Loads at
+// offsets outside the range return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ half8_t buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
+  return __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
+}
+
+// Buffer load of 16 bytes per lane straight into LDS: lane i's bytes land at
+// lds + 16 * i (one contiguous 1 KB block per wavefront; lds must be the
+// same for every lane).  Completion is counted by vmcnt.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, _Float16* lds, int offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, offset, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every buffer load of this wavefront, the copies into
+// LDS among them, has landed (lgkmcnt and expcnt left at their maximum)
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier that orders LDS accesses only.  The wavefronts of a
+// workgroup exchange data through LDS alone, so the barrier need not wait for
+// outstanding global loads or stores (__syncthreads() does: its workgroup
+// fence covers global memory too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 4 fp16 values through the transposing LDS read: in each 16-lane group,
+// lanes 4j..4j+3 read 16 consecutive halfs of row j and lane i receives
+// column i of rows 0..3.
+__device__ __forceinline__ short4_t lds_read_tr(const _Float16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+}
+
+// PV operand V^T[32 dims x 16 keys] for lane l: dims dt*32 + l%32, keys
+// 16c + 4*hf + (0..3) then 16c + 8 + 4*hf + (0..3) -- the key order of the
+// B operand taken straight from an S^T accumulator (registers 8(c%2)..+7 of
+// the 32-key block c/2).  `vl` already holds this lane's row/column offset.
+template <int VROW>
+__device__ __forceinline__ half8_t pv_operand(const _Float16* vl, int dt, int c) {
+  const short4_t lo = lds_read_tr(vl + 16 * c * VROW + dt * 32);
+  const short4_t hi = lds_read_tr(vl + (16 * c + 8) * VROW + dt * 32);
+  const short4_t lohi[2] = {lo, hi};
+  return __builtin_bit_cast(half8_t, lohi);
+}
+
+// Lane offset (halfs) of the transposed V read in a V tile of row stride
+// VROW: 16-lane group G = lane/16 covers dims 16*(G%2)..+15 of keys
+// 4*hf + (lane%16)/4, four dims per lane.
+template <int VROW>
+__device__ __forceinline__ int pv_lane_offset(int lane) {
+  const int hf = lane >> 5;
+  return (4 * hf + (lane & 15) / 4) * VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+}
+
+}  // namespace dev
+}  // namespace attn

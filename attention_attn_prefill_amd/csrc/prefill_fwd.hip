@@ -713,6 +713,7 @@ hipError_t launch_hp(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a_in, int head_dim, bool causal, hipStream_t stream) {
+  if (head_dim == 128 && !a_in.cos_table) return launch_prefill_dual(a_in, causal, stream);
   PrefillArgs a = a_in;
   a.n_qtiles = (a.S_q + kBlockM - 1) / kBlockM;
   switch (head_dim) {

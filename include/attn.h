@@ -69,8 +69,10 @@ const char* attn_status_string(attn_status_t status);
  * requires S_q == S_kv (the pages define causal prefill for one S only).
  * causal == 0: every row attends to all S_kv keys (cross-attention).
  * head_dim (D): 32, 64 or 128.  Any B, S_q, S_kv >= 1 (ragged tails are
- * masked inside the kernel), with S_kv * H_kv * D * 2 < 2^31 (one batch
- * entry's K or V below 2 GiB; larger is ATTN_ERR_UNSUPPORTED).
+ * masked inside the kernel), with (ceil(S_kv / 64) + 3) * 64 * H_kv * D * 2
+ * < 2^31 (one batch entry's K or V, rounded up to whole 64-key tiles plus
+ * three tiles of staging margin, below 2 GiB, so that 32-bit byte offsets
+ * reach it; larger is ATTN_ERR_UNSUPPORTED).
  */
 attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
                            int B, int S_q, int S_kv, int H_q, int H_kv,
