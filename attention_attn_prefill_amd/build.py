@@ -26,7 +26,9 @@ FLAGS = [
 # lowers to v_max3_f32 without canonicalising every MFMA result first.
 PER_FILE_FLAGS = {
     "prefill_fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
-    "prefill_dual.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+    # MFMA results in VGPRs: the score accumulators feed the softmax VALU
+    # directly (the Q fragments, pure MFMA operands, are pinned to AGPRs)
+    "prefill_dual.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -509,6 +509,10 @@ __device__ __forceinline__ void dual_qtile(const PrefillArgs& a, int qt, int hg,
 #pragma unroll
       for (int ks = 0; ks < W::KS; ++ks) w.qf[g][ks] = half8_t{};
     }
+    // the Q fragments are only ever MFMA operands: keep them in AGPRs so the
+    // score accumulators, which the softmax reads, fit in VGPRs
+#pragma unroll
+    for (int ks = 0; ks < W::KS; ++ks) asm volatile("" : "+a"(w.qf[g][ks]));
   }
 
   if (w.template run<false>(flags)) {
