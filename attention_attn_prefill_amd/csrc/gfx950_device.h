@@ -47,6 +47,14 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, _Flo
 // LDS among them, has landed (lgkmcnt and expcnt left at their maximum)
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): at most N of this wavefront's vector memory
+// operations outstanding (they complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Workgroup barrier that orders LDS accesses only.  The wavefronts of a
 // workgroup exchange data through LDS alone, so the barrier need not wait for
 // outstanding global loads or stores (__syncthreads() does: its workgroup

@@ -99,9 +99,11 @@ struct Dual {
   static constexpr int COPIES = K_COPIES + V_COPIES;
   static constexpr int ROWS_WG = HP == 2 ? 4 * 32 : 4 * 64;  // query rows per head and workgroup
   static constexpr int OROW = D + 8;                         // LDS row stride of the output tiles
+  static constexpr int OUT_LDS = 8 * 32 * OROW;               // output tiles, after the K/V slots and the spare block
+  static constexpr int SMEM_HALFS = LDS_HALFS + 512 + OUT_LDS;
   static_assert(K_BLOCKS * 1024 == kTile * KROW * 2 && V_BLOCKS * 1024 == kTile * VROW * 2,
                 "tiles must be whole 1 KB blocks");
-  static_assert(8 * 32 * OROW <= LDS_HALFS, "output tiles must fit the K/V tiles' LDS");
+  static_assert(SMEM_HALFS * 2 <= 160 * 1024, "LDS of one workgroup");
 
   _Float16* smem;
   int tid, lane, hf, col;
@@ -117,6 +119,8 @@ struct Dual {
   int mask_from;  // first sub-block that may need the element mask
   int n_tiles;    // K/V tiles the workgroup stages
   int row0[2];    // first query row of each row block
+  int head[2];    // query head of each row block
+  int b;          // batch entry
   half8_t qf[2][KS];
   f32x16_t o[2][DT];
   f32x16_t s[2][2];    // [sub-block parity][row block]
@@ -346,13 +350,19 @@ struct Dual {
     s[PP][1] = acc[1];
   }
 
-  // One pass over the keys.  KNOWN_REF: the references are the exact row
-  // maxima (cm already holds them); else the first sub-block sets them.
+  // One pass over the keys, with the Q fragments loaded and K(0), V(0),
+  // K(1) in LDS (published by a barrier).  KNOWN_REF: the references mb are
+  // the exact row maxima; else the first sub-block sets them.
   // Returns true when a row-sum share above kShareMax was seen anywhere in the
   // workgroup (workgroup-uniform).
   template <bool KNOWN_REF>
   __device__ __forceinline__ bool run(int* flags) {
-    stage_prologue();
+    // the Q fragments are only ever MFMA operands: keep them in AGPRs so the
+    // accumulators, which the softmax reads, fit in VGPRs
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qf[g][ks]));
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
 #pragma unroll
@@ -435,15 +445,131 @@ struct Dual {
 #pragma unroll
     for (int g = 0; g < 2; ++g) mb[g] = half_swap_max(m[g]) * c2;
   }
+
+  // ---- per query tile ------------------------------------------------------
+  // Geometry of query tile qt (the K/V side, same for every tile of the
+  // workgroup, is set up once by the kernel).
+  __device__ __forceinline__ void setup(const PrefillArgs& a, int qt, int hg) {
+    const int q0 = qt * ROWS_WG;
+    if (HP == 2) {
+      row0[0] = row0[1] = q0 + wave * 32;
+      head[0] = 2 * hg;
+      head[1] = 2 * hg + 1;
+    } else {
+      row0[0] = q0 + wave * 64;
+      row0[1] = row0[0] + 32;
+      head[0] = head[1] = hg;
+    }
+    const int kv_sub = (a.S_kv + 31) / 32;
+    int n_sub_wg;
+    if (CAUSAL) {
+      mask_from = row0[0] / 32;  // this wavefront's first diagonal sub-block
+      n_sub_wg = (min(q0 + ROWS_WG, a.S_q) - 1) / 32 + 1;
+    } else {
+      mask_from = (a.S_kv % 32) ? kv_sub - 1 : kv_sub;
+      n_sub_wg = kv_sub;
+    }
+    n_tiles = (n_sub_wg + 1) / 2;
+  }
+
+  // Q fragments (B operand of S^T = K Q^T: q[row][16*ks + 8*hf + 0..7])
+  // and the copies of K(0), V(0), K(1) into LDS; the caller waits for them.
+  // Loads per wavefront: 2 * KS for Q, 2 * K_COPIES + V_COPIES copies.
+  static constexpr int TILE_LOADS = 2 * KS + 2 * K_COPIES + V_COPIES;
+  __device__ __forceinline__ void issue_tile_loads(const PrefillArgs& a) {
+    const int64_t q_row_stride = (int64_t)a.H_q * D;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      // rows past S_q load row 0 (their results are never stored)
+      const int row = row0[g] + col < a.S_q ? row0[g] + col : 0;
+      const _Float16* qp = a.q + ((int64_t)b * a.S_q + row) * q_row_stride + (int64_t)head[g] * D + 8 * hf;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[g][ks] = *reinterpret_cast<const half8_t*>(qp + 16 * ks);
+    }
+    copy_tiles(0, 0);
+#pragma unroll
+    for (int n = 0; n < K_COPIES; ++n) copy(n, 1, 0);
+  }
+
+  // the whole query tile: first pass, and the recomputation when a
+  // row-sum share overflowed
+  __device__ __forceinline__ void compute(int* flags) {
+    if (run<false>(flags)) {
+      row_max_pass();
+      stage_prologue();
+      dev::lds_barrier();
+      run<true>(flags);
+    }
+  }
+
+  // Epilogue of a query tile (rows rows0, heads heads): normalise, round to
+  // fp16, and store whole rows through this wavefront's part of the output
+  // LDS.  Returns true when every row was stored (16 stores per wavefront,
+  // the count the caller may wait on), false for a ragged last tile.
+  __device__ __forceinline__ bool epilogue(const PrefillArgs& a, const int (&rows0)[2], const int (&heads)[2]) {
+    if (rows0[0] >= a.S_q) return false;
+    const int64_t q_row_stride = (int64_t)a.H_q * D;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float inv = 1.0f / half_swap_add(l[g]);
+      _Float16* ot = smem + LDS_HALFS + 512 + (wave * 2 + g) * 32 * OROW;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          half4_t out;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) out[j] = (_Float16)(o[g][dt][rg * 4 + j] * inv);
+          *reinterpret_cast<half4_t*>(ot + col * OROW + dt * 32 + rg * 8 + hf * 4) = out;
+        }
+      }
+    }
+    // the lanes read rows that other lanes of this wavefront wrote
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    constexpr int PIECES = D / 8;          // 16-byte pieces per row
+    constexpr int ROWS_PER = 64 / PIECES;  // rows per 64-lane store
+    const int pr = lane / PIECES, pc = lane % PIECES;
+    const bool full = rows0[1] + 31 < a.S_q;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const _Float16* ot = smem + LDS_HALFS + 512 + (wave * 2 + g) * 32 * OROW;
+#pragma unroll
+      for (int i = 0; i < 32 / ROWS_PER; ++i) {
+        const int r = i * ROWS_PER + pr;
+        const int row = rows0[g] + r;
+        const half8_t v8 = *reinterpret_cast<const half8_t*>(ot + r * OROW + 8 * pc);
+        if (full || row < a.S_q)
+          *reinterpret_cast<half8_t*>(a.o + ((int64_t)b * a.S_q + row) * q_row_stride + (int64_t)heads[g] * D + 8 * pc) = v8;
+      }
+    }
+    return full;
+  }
 };
 
-// One query tile (ROWS_WG rows of each of the HP heads of head group hg,
-// batch b) against its keys.
+// Work unit of a workgroup: query tiles qt and n_qtiles-1-qt of one (head
+// group, batch).  Under the causal mask tile i costs i+1 units of keys, so
+// every pair costs the same and the grid has no long-tile tail; an odd
+// middle tile runs alone.  Both tiles read the same kv head, so the K/V side
+// is set up once.  The second tile's Q loads and first K/V copies go out
+// before the first tile's epilogue, which then overlaps their latency.
 template <bool CAUSAL, int HP>
-__device__ __forceinline__ void dual_qtile(const PrefillArgs& a, int qt, int hg, int b, _Float16* smem,
-                                           int* flags) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a) {
   using W = Dual<CAUSAL, HP>;
   constexpr int D = W::D;
+  __shared__ __attribute__((aligned(16))) _Float16 smem[W::SMEM_HALFS];
+  __shared__ int flags[kWaves];
+  const int head_groups = a.H_q / HP;
+  const int combos = head_groups * a.B;
+  // the raw work-group / work-item id builtins: this file is built without
+  // NaN semantics, so the device library's blockIdx / threadIdx helpers
+  // (built with them) are not inlined and would become calls
+  const int id = (int)__builtin_amdgcn_workgroup_id_x();
+  const int pair = id / combos;
+  const int rem = id - pair * combos;
+  const int hg = rem % head_groups;
+  const int lo = pair, hi = a.n_qtiles - 1 - pair;
+
   W w;
   w.smem = smem;
   w.tid = (int)__builtin_amdgcn_workitem_id_x();
@@ -451,43 +577,17 @@ __device__ __forceinline__ void dual_qtile(const PrefillArgs& a, int qt, int hg,
   // the wavefront index is uniform; readfirstlane lets the compiler see that,
   // so everything derived from it (row blocks, sub-block counts) is scalar
   w.wave = __builtin_amdgcn_readfirstlane(w.tid >> 6);
-  const int wave = w.wave;
   w.col = w.lane & 31;
   w.hf = w.lane >> 5;
   w.S_kv = a.S_kv;
-
-  const int q0 = qt * W::ROWS_WG;
-  int head[2];
-  if (HP == 2) {
-    const int qw = q0 + wave * 32;
-    w.row0[0] = w.row0[1] = qw;
-    head[0] = 2 * hg;
-    head[1] = 2 * hg + 1;
-  } else {
-    const int qw = q0 + wave * 64;
-    w.row0[0] = qw;
-    w.row0[1] = qw + 32;
-    head[0] = head[1] = hg;
-  }
-  const int g_kv = (int)(((int64_t)hg * HP * a.H_kv) / a.H_q);
-
-  // sub-blocks of this wavefront and of the workgroup
-  const int kv_sub = (a.S_kv + 31) / 32;
-  int n_sub_wg;
-  if (CAUSAL) {
-    w.mask_from = w.row0[0] / 32;  // this wavefront's first diagonal sub-block
-    n_sub_wg = (min(q0 + W::ROWS_WG, a.S_q) - 1) / 32 + 1;
-  } else {
-    w.mask_from = (a.S_kv % 32) ? kv_sub - 1 : kv_sub;
-    n_sub_wg = kv_sub;
-  }
-  w.n_tiles = (n_sub_wg + 1) / 2;
-
+  w.b = rem / head_groups;
+  w.c2 = a.scale_log2;
   w.k_lane = w.col * W::KROW + 8 * w.hf;
   w.v_lane = dev::pv_lane_offset<W::VROW>(w.lane);
+  const int g_kv = (int)(((int64_t)hg * HP * a.H_kv) / a.H_q);
   const int64_t kv_row_stride = (int64_t)a.H_kv * D;
-  const _Float16* kbase = a.k + (int64_t)b * a.S_kv * kv_row_stride + (int64_t)g_kv * D;
-  const _Float16* vbase = a.v + (int64_t)b * a.S_kv * kv_row_stride + (int64_t)g_kv * D;
+  const _Float16* kbase = a.k + (int64_t)w.b * a.S_kv * kv_row_stride + (int64_t)g_kv * D;
+  const _Float16* vbase = a.v + (int64_t)w.b * a.S_kv * kv_row_stride + (int64_t)g_kv * D;
   w.row_bytes = (uint32_t)kv_row_stride * 2u;
   const int range = (int)((uint32_t)a.S_kv * w.row_bytes);  // host guarantees < 2^31
   w.krsrc = dev::make_rsrc(kbase, range);
@@ -495,86 +595,24 @@ __device__ __forceinline__ void dual_qtile(const PrefillArgs& a, int qt, int hg,
   w.template copy_offsets<W::KROW>(w.k_off, W::K_COPIES);
   w.template copy_offsets<W::VROW>(w.v_off, W::V_COPIES);
 
-  // Q fragments (B operand of S^T = K Q^T): q[row][16*ks + 8*hf + 0..7]
-  const int64_t q_row_stride = (int64_t)a.H_q * D;
-  w.c2 = a.scale_log2;
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int row = w.row0[g] + w.col;
-    if (row < a.S_q) {
-      const _Float16* qp = a.q + ((int64_t)b * a.S_q + row) * q_row_stride + (int64_t)head[g] * D + 8 * w.hf;
-#pragma unroll
-      for (int ks = 0; ks < W::KS; ++ks) w.qf[g][ks] = *reinterpret_cast<const half8_t*>(qp + 16 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < W::KS; ++ks) w.qf[g][ks] = half8_t{};
-    }
-    // the Q fragments are only ever MFMA operands: keep them in AGPRs so the
-    // score accumulators, which the softmax reads, fit in VGPRs
-#pragma unroll
-    for (int ks = 0; ks < W::KS; ++ks) asm volatile("" : "+a"(w.qf[g][ks]));
-  }
-
-  if (w.template run<false>(flags)) {
-    w.row_max_pass();
-    w.template run<true>(flags);
-  }
-
-  // epilogue: normalise, round to fp16, and store whole rows through this
-  // wavefront's own part of the (now idle) K/V tiles' LDS
-  if (w.row0[0] >= a.S_q) return;
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const float inv = 1.0f / half_swap_add(w.l[g]);
-    _Float16* ot = smem + (wave * 2 + g) * 32 * W::OROW;
-#pragma unroll
-    for (int dt = 0; dt < W::DT; ++dt) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        half4_t out;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = (_Float16)(w.o[g][dt][rg * 4 + j] * inv);
-        *reinterpret_cast<half4_t*>(ot + w.col * W::OROW + dt * 32 + rg * 8 + w.hf * 4) = out;
-      }
-    }
-  }
-  // the lanes read rows that other lanes of this wavefront wrote
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  constexpr int PIECES = D / 8;          // 16-byte pieces per row
-  constexpr int ROWS_PER = 64 / PIECES;  // rows per 64-lane store
-  const int pr = w.lane / PIECES, pc = w.lane % PIECES;
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const _Float16* ot = smem + (wave * 2 + g) * 32 * W::OROW;
-#pragma unroll
-    for (int i = 0; i < 32 / ROWS_PER; ++i) {
-      const int r = i * ROWS_PER + pr;
-      const int row = w.row0[g] + r;
-      const half8_t v8 = *reinterpret_cast<const half8_t*>(ot + r * W::OROW + 8 * pc);
-      if (row < a.S_q)
-        *reinterpret_cast<half8_t*>(a.o + ((int64_t)b * a.S_q + row) * q_row_stride + (int64_t)head[g] * D + 8 * pc) = v8;
-    }
-  }
-}
-
-template <bool CAUSAL, int HP>
-__global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 smem[Dual<CAUSAL, HP>::LDS_HALFS + 512];
-  __shared__ int flags[kWaves];
-  const int head_groups = a.H_q / HP;
-  const int combos = head_groups * a.B;
-  const int id = (int)__builtin_amdgcn_workgroup_id_x();
-  const int pair = id / combos;
-  const int rem = id - pair * combos;
-  const int hg = rem % head_groups;
-  const int b = rem / head_groups;
-  const int lo = pair, hi = a.n_qtiles - 1 - pair;
-  dual_qtile<CAUSAL, HP>(a, hi, hg, b, smem, flags);
+  w.setup(a, hi, hg);
+  w.issue_tile_loads(a);
+  dev::wait_vmcnt0();
+  dev::lds_barrier();
+  w.compute(flags);
   if (lo < hi) {
-    dev::lds_barrier();  // the first tile's epilogue reads are done
-    dual_qtile<CAUSAL, HP>(a, lo, hg, b, smem, flags);
+    // the K/V slots are free (the last pass ended with a barrier) and the Q
+    // fragments dead: start the second tile's loads, then store the first
+    const int rows0[2] = {w.row0[0], w.row0[1]};
+    const int heads[2] = {w.head[0], w.head[1]};
+    w.setup(a, lo, hg);
+    w.issue_tile_loads(a);
+    if (w.epilogue(a, rows0, heads)) dev::wait_vmcnt<2 * (D / 8) * 32 / 64>();  // its 16 stores may stay in flight
+    else dev::wait_vmcnt0();
+    dev::lds_barrier();
+    w.compute(flags);
   }
+  w.epilogue(a, w.row0, w.head);
 }
 
 template <bool CAUSAL, int HP>
