@@ -14,13 +14,17 @@ Recipe:
     ``num_blocks = sum(ceil(L/16))``; physical ids are a seeded permutation of
     ``0..num_blocks-1`` handed out in (sequence, logical block) order; unused
     table entries are -1.
-  * the cross-attention attention core (cross_attn) takes plain normal
-    Q/K/V; the rotary embedding of that workload belongs to the module
-    (x_q, x_kv and nn.Linear-style uniform weights from
-    ``cross_module_inputs``), which each side rotates with its own code.
-  * the pages' own unit-test inputs ("Tutorial: Adding a New Kernel to
-    RL.cu", test_attention.cu: the deterministic LCG helper and the test
-    runners) are reproduced by ``pages_prefill_case`` / ``pages_decode_case``.
+  * the cross-attention attention core (cross_attn): normal Q/K/V from
+    here; the tests rotate Q and K by adjacent-pair RoPE (base 10000,
+    positions 0..T-1) with the oracle's fp64 rotation and round them to
+    binary16, so both sides consume the same rotated inputs (this module
+    holds no arithmetic).  The full cross-attention module draws x_q, x_kv
+    and nn.Linear-style uniform weights from ``cross_module_inputs``.
+  * the pages' own unit-test shapes ("Tutorial: Adding a New Kernel to
+    RL.cu", test_attention.cu: the case list and the value range
+    [-0.5, 0.5)) get uniform inputs from ``pages_prefill_case`` /
+    ``pages_decode_case`` (this module's PCG64 draws, not the pages' own
+    generator).
 """
 from __future__ import annotations
 
@@ -247,47 +251,33 @@ def kv_bytes(seq_lens, H_kv: int, D: int) -> int:
     return int(np.maximum(np.asarray(seq_lens, np.int64), 0).sum()) * H_kv * D * 2 * 2
 
 
-# ---- the pages' own unit-test inputs ---------------------------------------
+# ---- inputs for the pages' own unit-test shapes ----------------------------
 
-class PagesLCG:
-    """The 32-bit LCG of the pages' attention unit test (multiplier 1664525,
-    increment 1013904223, state 42), mapped to [-1, 1] in float32."""
-
-    def __init__(self, state: int = 42):
-        self.state = state & 0xFFFFFFFF
-
-    def uniform(self, n: int) -> np.ndarray:
-        states = np.empty(n, np.uint32)
-        s = self.state
-        for i in range(n):
-            s = (s * 1664525 + 1013904223) & 0xFFFFFFFF
-            states[i] = s
-        self.state = s
-        x = (states >> np.uint32(1)).astype(np.float32) / np.float32(0x7FFFFFFF)
-        return x * np.float32(2.0) - np.float32(1.0)
+def uniform_f16(shape, seed_words, lo: float = -0.5, hi: float = 0.5) -> np.ndarray:
+    """Uniform [lo, hi) binary16 array (PCG64, deterministic in seed_words)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(seed_words))))
+    return g.uniform(lo, hi, int(np.prod(shape))).astype(np.float16).reshape(shape)
 
 
-def pages_prefill_case(lcg: PagesLCG, B: int, S: int, H_q: int, H_kv: int, D: int = 128):
-    """Q, K, V as the pages' prefill test draws them: U(-0.5, 0.5) in float32
-    from the shared LCG, Q then K then V, rounded to binary16."""
-    half = np.float32(0.5)
-    q = (lcg.uniform(B * S * H_q * D) * half).astype(np.float16).reshape(B, S, H_q, D)
-    k = (lcg.uniform(B * S * H_kv * D) * half).astype(np.float16).reshape(B, S, H_kv, D)
-    v = (lcg.uniform(B * S * H_kv * D) * half).astype(np.float16).reshape(B, S, H_kv, D)
+def pages_prefill_case(case: int, B: int, S: int, H_q: int, H_kv: int, D: int = 128):
+    """Q, K, V at one of the pages' prefill unit-test shapes, with values
+    uniform in [-0.5, 0.5) like the pages' cases (drawn from this module's
+    own PCG64 generator, seeded by the case number)."""
+    q = uniform_f16((B, S, H_q, D), (10, case, 0))
+    k = uniform_f16((B, S, H_kv, D), (10, case, 1))
+    v = uniform_f16((B, S, H_kv, D), (10, case, 2))
     return q, k, v
 
 
-def pages_decode_case(lcg: PagesLCG, num_seqs: int, ctx: int, H_q: int, H_kv: int,
+def pages_decode_case(case: int, num_seqs: int, ctx: int, H_q: int, H_kv: int,
                       D: int = 128, block_size: int = 16):
-    """The pages' decode test: q, then K and V drawn alternately per element
-    into a contiguous [num_seqs, ctx, H_kv, D] context, paged with the identity
-    table (sequence s, logical block b -> physical s*blocks_per_seq + b)."""
-    half = np.float32(0.5)
-    q = (lcg.uniform(num_seqs * H_q * D) * half).astype(np.float16).reshape(num_seqs, H_q, D)
-    n = num_seqs * ctx * H_kv * D
-    kv = lcg.uniform(2 * n) * half
-    k = kv[0::2].astype(np.float16).reshape(num_seqs, ctx, H_kv, D)
-    v = kv[1::2].astype(np.float16).reshape(num_seqs, ctx, H_kv, D)
+    """One of the pages' decode unit-test shapes: q and a contiguous
+    [num_seqs, ctx, H_kv, D] context uniform in [-0.5, 0.5), paged with the
+    identity table (sequence s, logical block b -> physical s*blocks_per_seq
+    + b), as the pages' decode test lays it out."""
+    q = uniform_f16((num_seqs, H_q, D), (11, case, 0))
+    k = uniform_f16((num_seqs, ctx, H_kv, D), (11, case, 1))
+    v = uniform_f16((num_seqs, ctx, H_kv, D), (11, case, 2))
     bps = (ctx + block_size - 1) // block_size
     k_cache = np.zeros((num_seqs * bps, H_kv, block_size, D), np.float16)
     v_cache = np.zeros_like(k_cache)
@@ -347,7 +337,7 @@ def ceil_div(a: int, b: int) -> int:
 
 __all__ = [
     "PrefillConfig", "DecodeConfig", "CONFIGS", "normal_f16", "cross_module_inputs", "forked_decode_inputs", "grpo_decode_inputs", "GRPO_DECODE",
-    "prefill_inputs", "decode_inputs", "paged_layout", "kv_bytes", "PagesLCG",
+    "prefill_inputs", "decode_inputs", "paged_layout", "kv_bytes", "uniform_f16",
     "pages_prefill_case", "pages_decode_case", "paginate", "sample_prefill_rows",
     "expected_pairs_decode", "ceil_div",
 ]

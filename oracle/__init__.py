@@ -69,6 +69,8 @@ class Oracle:
         lib.oracle_qk_norm_rope.restype = I
         lib.oracle_cross_attention.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D_, P]
         lib.oracle_cross_attention.restype = I
+        lib.oracle_rope_interleaved.argtypes = [P, I64, I64, I, I, D_, P]
+        lib.oracle_rope_interleaved.restype = I
         self._lib = lib
         return lib
 
@@ -214,6 +216,18 @@ class Oracle:
         return out
 
 
+    def rope_interleaved(self, x, base: float = 10000.0):
+        """Interleaved-pair rotary embedding of x [B, T, H, D] (float16): pair
+        (2j, 2j+1) of row t turns by t * base^(-2j/D).  Returns float64."""
+        x = _f16(x)
+        B, T, H, D = x.shape
+        out = np.empty((B, T, H, D), np.float64)
+        rc = self._load().oracle_rope_interleaved(_ptr(x), B, T, H, D, float(base), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_rope_interleaved rejected its arguments")
+        return out
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -234,3 +248,4 @@ kv_append = default.kv_append
 rope_table = default.rope_table
 qk_norm_rope = default.qk_norm_rope
 cross_attention = default.cross_attention
+rope_interleaved = default.rope_interleaved

@@ -393,6 +393,38 @@ int oracle_qk_norm_rope(const uint16_t* x, const uint16_t* weight, const int32_t
   return 0;
 }
 
+/* ---- interleaved-pair rotary embedding ---------------------------------- */
+/* The rotation of the cross-attention trace (POPCORNBENCH "Kimi-K2.6" page,
+ * its RoPE discussion): adjacent pairs (2j, 2j+1) of every head turn by the
+ * angle pos * base^(-2j/D), pos being the row's index in its sequence:
+ *     r_{2j}   = u_{2j} cos - u_{2j+1} sin
+ *     r_{2j+1} = u_{2j} sin + u_{2j+1} cos
+ * x: [B, T, H, D] binary16 (row t of every batch entry is at position t);
+ * out: fp64 [B, T, H, D].  The non-causal cross-attention workload feeds Q
+ * and K through this rotation (base 10000) before attention; the fp64
+ * result is rounded to binary16 by the caller.
+ * Returns 0, or -1 on invalid arguments.                                     */
+int oracle_rope_interleaved(const uint16_t* x, int64_t B, int64_t T, int H, int D, double base,
+                            double* out) {
+  if (!x || !out || B < 0 || T < 0 || H <= 0 || D <= 0 || (D & 1) || !(base > 0.0)) return -1;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t t = 0; t < T; ++t) {
+      for (int h = 0; h < H; ++h) {
+        const int64_t row = ((b * T + t) * H + h) * (int64_t)D;
+        for (int j = 0; j < D / 2; ++j) {
+          const double ang = (double)t * pow(base, -2.0 * (double)j / (double)D);
+          const double c = cos(ang), sn = sin(ang);
+          const double u0 = half_bits_to_double(x[row + 2 * j]);
+          const double u1 = half_bits_to_double(x[row + 2 * j + 1]);
+          out[row + 2 * j] = u0 * c - u1 * sn;
+          out[row + 2 * j + 1] = u0 * sn + u1 * c;
+        }
+      }
+    }
+  }
+  return 0;
+}
+
 /* ---- cross-attention module with RoPE --------------------------------------- */
 /* The module of the cross-attention trace (POPCORNBENCH "Kimi-K2.6" page, the
  * problem statement and its nn.Linear notes): one layer of multi-head

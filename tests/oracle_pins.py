@@ -33,6 +33,10 @@ What pins what:
   * QK RMSNorm               -- unit mean square, scale invariance, a
                                 constant-row closed form (mean, eps, weight);
                                 numpy RMSNorm then rotation (the pages' order)
+  * interleaved-pair rotation (the cross-attention workload's Q and K)
+                             -- numpy complex multiplication of adjacent
+                                pairs; position 0 is the identity; norms
+                                kept; only the position offset matters
   * cross-attention module   -- torch fp64 (F.linear, complex RoPE, SDPA);
                                 identical memory rows; a single key
   * forked (shared-prefix) decode -- tables sharing the prompt's blocks
@@ -250,8 +254,8 @@ def pin_matches_torch_sdpa(ora):
         v = _rand16((B, S_kv, H_kv, D), 50 + i)
         o = ora.prefill(q, k, v, causal=causal)
         assert np.allclose(o, _torch_sdpa(q, k, v, causal), rtol=1e-12, atol=1e-13), i
-    # the pages' own first unit-test case (LCG inputs, B=1 S=16 H 2/1)
-    q, k, v = W.pages_prefill_case(W.PagesLCG(42), 1, 16, 2, 1)
+    # the pages' first unit-test shape (B=1 S=16 H 2/1), uniform inputs
+    q, k, v = W.pages_prefill_case(0, 1, 16, 2, 1)
     assert np.allclose(ora.prefill(q, k, v, True), _torch_sdpa(q, k, v, True),
                        rtol=1e-12, atol=1e-13)
 
@@ -536,6 +540,48 @@ def pin_rope_rejects_invalid(ora):
 
 
 # ---- cross-attention module with interleaved-pair RoPE ------------------------
+
+def _np_rotate_adjacent(x, base):
+    """Adjacent-pair rotation as a complex product: (x_{2j} + i*x_{2j+1}) *
+    exp(i*t*inv_freq_j) for row t of [B, T, H, D], numpy complex arithmetic."""
+    B, T, H, D = x.shape
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    ang = np.arange(T, dtype=np.float64)[None, :, None, None] * _np_inv_freq(D, base)[None, None, None, :]
+    r = z * np.exp(1j * ang)
+    out = np.empty(x.shape, np.float64)
+    out[..., 0::2], out[..., 1::2] = r.real, r.imag
+    return out
+
+
+def pin_rope_interleaved_matches_complex_rotation(ora):
+    """The cross-attention workload's rotation (adjacent pairs, base 1e4)
+    equals numpy's complex product, at its own shapes and at D = 128."""
+    for shape, base in (((4, 64, 8, 32), 1e4), ((4, 128, 8, 32), 1e4), ((2, 300, 2, 128), 1e6)):
+        x = _rand16(shape, 230 + shape[1])
+        assert np.allclose(ora.rope_interleaved(x, base), _np_rotate_adjacent(_f64(x), base), rtol=0, atol=1e-12)
+
+
+def pin_rope_interleaved_identity_norm_and_offset(ora):
+    """Row 0 is unrotated (bitwise); every pair keeps its length; and the dot
+    product of rows m and n of two rotated tensors depends on m - n only."""
+    x = _rand16((1, 96, 2, 64), 240)
+    r = ora.rope_interleaved(x)
+    assert np.array_equal(r[:, 0], _f64(x)[:, 0])
+    pn = lambda a: np.hypot(a[..., 0::2], a[..., 1::2])
+    assert np.allclose(pn(r), pn(_f64(x)), rtol=1e-14, atol=0)
+    # the same vector at every position: <R(m) q, R(n) k> depends on m - n
+    q = np.broadcast_to(_rand16((1, 1, 1, 64), 241), (1, 96, 1, 64)).copy()
+    k = np.broadcast_to(_rand16((1, 1, 1, 64), 242), (1, 96, 1, 64)).copy()
+    rq, rk = ora.rope_interleaved(q)[0, :, 0], ora.rope_interleaved(k)[0, :, 0]
+    for m, n, d in ((5, 2, 40), (80, 10, -9), (0, 0, 95)):
+        assert np.isclose(rq[m] @ rk[n], rq[m + d] @ rk[n + d], rtol=1e-12, atol=1e-12)
+
+
+def pin_rope_interleaved_rejects_invalid(ora):
+    import pytest
+    with pytest.raises(ValueError):
+        ora.rope_interleaved(_rand16((1, 2, 1, 7), 243))
+
 
 def _module_inputs(B, T_q, T_k, dim, seed):
     rng = np.random.default_rng(seed)

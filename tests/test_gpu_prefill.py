@@ -30,8 +30,15 @@ def _rand(shape, seed, scale=1.0):
 
 @pytest.mark.parametrize("name", ["tiny_causal", "cross_attn"])
 def test_small_configs_full(name):
+    """Every output element of the two small configurations.  The
+    cross-attention core takes Q and K rotated by adjacent-pair RoPE (base
+    10000, positions 0..T-1), done in fp64 by the oracle and rounded to fp16,
+    so both sides see the same rotated inputs."""
     cfg = W.CONFIGS[name]
     q, k, v = W.prefill_inputs(cfg)
+    if name == "cross_attn":
+        q = oracle.rope_interleaved(q, 1e4).astype(np.float16)
+        k = oracle.rope_interleaved(k, 1e4).astype(np.float16)
     say(name, q.shape, k.shape)
     got = gpu_prefill(q, k, v, cfg.causal)
     ref = oracle.prefill(q, k, v, cfg.causal)
@@ -39,13 +46,13 @@ def test_small_configs_full(name):
 
 
 def test_pages_unit_cases():
-    """The pages' unit-test shapes and LCG inputs; their pass criterion was a
-    max absolute error below 5e-3, and their kernels reached about 1.2e-4."""
-    lcg = W.PagesLCG(42)
-    for kind, B, S, H_q, H_kv, D in pages_cases():
+    """The pages' unit-test shapes with inputs uniform in [-0.5, 0.5); their
+    pass criterion was a max absolute error below 5e-3, and their kernels
+    reached about 1.2e-4."""
+    for case, (kind, B, S, H_q, H_kv, D) in enumerate(pages_cases()):
         if kind != "prefill":
             continue
-        q, k, v = W.pages_prefill_case(lcg, B, S, H_q, H_kv, D)
+        q, k, v = W.pages_prefill_case(case, B, S, H_q, H_kv, D)
         say("pages prefill", B, S, H_q, H_kv, D)
         err = assert_parity(gpu_prefill(q, k, v, True), oracle.prefill(q, k, v, True), "pages")
         assert err < 5e-3
@@ -115,14 +122,16 @@ def test_increasing_logits():
     assert_parity(gpu_prefill(q, k, v, True), oracle.prefill(q, k, v, True), "increasing")
 
 
-def test_qwen3_prefill_full_size_sampled_rows():
+@pytest.mark.timeout(300)
+def test_qwen3_prefill_full_size_every_element():
+    """The Qwen3-shaped prefill (B=4, S=2048, 16/8 heads, D=128, causal) at
+    full size, every output element against the fp64 oracle."""
     cfg = W.CONFIGS["qwen3_prefill"]
     q, k, v = W.prefill_inputs(cfg)
     say("qwen3_prefill full size")
-    got = gpu_prefill(q, k, v, True).reshape(-1, cfg.D)
-    rows = W.sample_prefill_rows(cfg, 3000)
-    ref = oracle.prefill(q, k, v, True, rows=rows)
-    assert_parity(got[rows], ref, "qwen3_prefill")
+    got = gpu_prefill(q, k, v, True)
+    ref = oracle.prefill(q, k, v, True)
+    assert_parity(got, ref, "qwen3_prefill")
 
 
 @pytest.mark.timeout(600)

@@ -49,6 +49,9 @@ MUTANTS = [
     ("rmsnorm: eps outside the root", "sqrt(ss / (double)D + eps)", "(sqrt(ss / (double)D) + eps)"),
     ("rmsnorm: sum instead of mean", "sqrt(ss / (double)D + eps)", "sqrt(ss + eps)"),
     ("rmsnorm: weight dropped", "y[d] = y[d] / r * half_bits_to_double(weight[d]);", "y[d] = y[d] / r;"),
+    ("interleaved rope: sine sign flipped", "out[row + 2 * j] = u0 * c - u1 * sn;", "out[row + 2 * j] = u0 * c + u1 * sn;"),
+    ("interleaved rope: position off by one", "const double ang = (double)t * pow(base, -2.0 * (double)j / (double)D);",
+     "const double ang = (double)(t + 1) * pow(base, -2.0 * (double)j / (double)D);"),
     ("module: NeoX pairs instead of adjacent ones", "const double a = u[2 * j], b = u[2 * j + 1];",
      "const double a = u[j], b = u[j + D / 2];"),
     ("module: x W instead of x W^T", "half_bits_to_double(w_q[(int64_t)c * dim + e])",
