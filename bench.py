@@ -12,9 +12,18 @@ own), which the default line also carries as ``shared_prefix_decode``.
 
 Prints one JSON line.  ``value`` is prefill TFLOP/s (exact unmasked-pair flop
 count, 4*D per pair); the decode half of the metric (KV GB/s: K and V bytes
-of every visible token) is in ``decode``.  Per-kernel durations come from HIP
-events recorded on the stream the kernels run on.  ``cpu_baseline`` times
-the fp64 CPU oracle on a bounded sample of the same workload.
+of every visible token) is in ``decode``.
+
+Timing.  After the ``--warmup`` steps the same step keeps running until at
+least one second of GPU work has passed (clocks settle; a handful of steps
+is not enough), then exactly ``--steps`` steps are timed.  HIP events on the
+launch stream bracket each prefill and each decode call; ``value`` uses the
+median prefill duration over the timed steps, ``roofline.achieved`` the mean,
+and both are in the line with the min and max.  ``pages_method`` repeats the
+measurement the way the pages' benchmark harness does it: events around 200
+back-to-back launches after 10 warm-up launches, median of 5 repeats.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -38,7 +47,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=["qwen3", "long", "grpo"], default="qwen3")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile", action="store_true",
@@ -52,7 +61,11 @@ def parse():
 
 
 KERNEL_SOURCES = {
+    "prefill_dual_kernel": ["attention_attn_prefill_amd/csrc/prefill_dual.hip",
+                            "attention_attn_prefill_amd/csrc/gfx950_device.h",
+                            "attention_attn_prefill_amd/csrc/attn_internal.h"],
     "prefill_fwd_kernel": ["attention_attn_prefill_amd/csrc/prefill_fwd.hip",
+                           "attention_attn_prefill_amd/csrc/gfx950_device.h",
                            "attention_attn_prefill_amd/csrc/attn_internal.h"],
     "decode_split_kernel": ["attention_attn_prefill_amd/csrc/decode_paged.hip",
                             "attention_attn_prefill_amd/csrc/attn_internal.h"],
@@ -127,12 +140,66 @@ def cpu_baseline(pcfg, dcfg, q, k, v, dq, kc, vc, bt, sl, target_s):
             break
     return {
         "value": flops / tp / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        "nproc": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"prefill: {n} of {n_rows_total} query rows (uniform random, "
                   f"{pairs_of(rows)} unmasked pairs) in {tp:.2f} s; decode: {len(picked)} of "
                   f"{dcfg.num_seqs} sequences in {spent:.2f} s",
         "decode": {"value": kvb / spent / 1e9, "unit": "GB/s"},
     }
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def profile_kernel_us(workload: str, kernel_prefix: str):
+    """Average duration (us) of a kernel in the committed kernel-trace
+    summary profiles/kernel_stats_<workload>.md, or None."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        cells = [c.strip() for c in line.split("|")]
+        # | `kernel name` | calls | average (us) | min | max | share |
+        if len(cells) > 4 and re.search(r"::" + re.escape(kernel_prefix) + r"[<(]", cells[1]):
+            try:
+                return float(cells[3])
+            except ValueError:
+                return None
+    return None
+
+
+def stats_ms(xs):
+    xs = np.asarray(xs, np.float64)
+    return {"median": round(float(np.median(xs)), 5), "mean": round(float(xs.mean()), 5),
+            "min": round(float(xs.min()), 5), "max": round(float(xs.max()), 5)}
+
+
+def pages_method(fn, stream, iters=200, warm=10, repeats=5):
+    """The pages' benchmark harness: events around `iters` back-to-back
+    launches after `warm` warm-up launches; the median of `repeats` runs (ms
+    per launch)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    res = []
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) / iters)
+    return float(np.median(res)), res
 
 
 def time_kv_append(pcfg, k, v, dev, stream, W, traffic_key, iters=100):
@@ -445,19 +512,35 @@ def main():
         args.no_cpu_baseline = True
         calibration_copy(dev)
 
+    def prefill():
+        attn_prefill(tq, tk, tv, to, causal=pcfg.causal, stream=stream)
+
+    def decode():
+        attn_decode_paged(tdq, tkc, tvc, tout, tbt, tsl, workspace=ws, stream=stream)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        attn_prefill(tq, tk, tv, to, causal=pcfg.causal, stream=stream)
+        prefill()
         if ev is not None:
             ev[1].record(stream)
-        attn_decode_paged(tdq, tkc, tvc, tout, tbt, tsl, workspace=ws, stream=stream)
+        decode()
         if ev is not None:
             ev[2].record(stream)
 
+    # warm-up: the requested steps, then more until a second of GPU work has
+    # passed (the clocks of a freshly idle GPU take that long to settle)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    extra_warm = 0
+    while time.perf_counter() - t_warm < 1.0:
+        for _ in range(4):
+            step()
+        extra_warm += 4
+        torch.cuda.synchronize()
+
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     if torch.distributed.is_available() and torch.distributed.is_initialized():
         torch.distributed.barrier()
@@ -467,19 +550,38 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] timed {args.steps} steps (after {args.warmup} + {extra_warm} warm-up steps)",
+          file=sys.stderr, flush=True)
 
-    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    pre = [e[0].elapsed_time(e[1]) for e in events]
+    dec = [e[1].elapsed_time(e[2]) for e in events]
+    pre_st, dec_st = stats_ms(pre), stats_ms(dec)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     flops = pcfg.flops
-    pre_tflops = flops / (pre_ms * 1e-3) / 1e12
     kvb = W.kv_bytes(sl, dcfg.H_kv, dcfg.D)
-    dec_gbs = kvb / (dec_ms * 1e-3) / 1e9
+    pre_tflops = flops / (pre_st["median"] * 1e-3) / 1e12
+    pre_tflops_mean = flops / (pre_st["mean"] * 1e-3) / 1e12
+    dec_gbs = kvb / (dec_st["median"] * 1e-3) / 1e9
+    dec_gbs_mean = kvb / (dec_st["mean"] * 1e-3) / 1e9
+
+    # the pages' harness: 200 back-to-back launches, median of 5 repeats
+    if args.profile:
+        pm = None
+    else:
+        pm_pre, pm_pre_all = pages_method(prefill, stream)
+        pm_dec, pm_dec_all = pages_method(decode, stream)
+        pm = {"what": "HIP events around 200 back-to-back launches after 10 warm-up launches, median of 5 repeats",
+              "prefill_ms": round(pm_pre, 5), "prefill_repeats_ms": [round(x, 5) for x in pm_pre_all],
+              "prefill_tflops": round(flops / (pm_pre * 1e-3) / 1e12, 2),
+              "decode_ms": round(pm_dec, 5), "decode_repeats_ms": [round(x, 5) for x in pm_dec_all],
+              "decode_gbs": round(kvb / (pm_dec * 1e-3) / 1e9, 1)}
 
     traffic_key = f"{pname}_{dname}"
     pcfg_bytes = 2 * (q.size + k.size + v.size + q.size)
+    pre_kernel = "prefill_dual_kernel" if pcfg.D == 128 else "prefill_fwd_kernel"
+    split_us = profile_kernel_us(traffic_key, "decode_split_kernel")
+    merge_us = profile_kernel_us(traffic_key, "decode_merge_kernel")
     line = {
         "metric": "prefill TFLOP/s + paged-decode KV GB/s (Qwen3-0.6B shapes), % of roofline",
         "value": round(pre_tflops, 2),
@@ -487,6 +589,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "extra_warmup_steps": extra_warm,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -504,24 +607,31 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "mfma", "kernel": "prefill_fwd_kernel<128,causal>",
-            "achieved": round(pre_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(pre_tflops / PEAK_FP16_TFLOPS, 4),
-            "traffic": measured_traffic(traffic_key, "prefill_fwd_kernel"),
+            "bound": "mfma", "kernel": f"{pre_kernel}<{pcfg.D},causal>",
+            "achieved": round(pre_tflops_mean, 2), "achieved_from": "mean launch duration over the timed steps",
+            "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(pre_tflops_mean / PEAK_FP16_TFLOPS, 4),
+            "frac_median": round(pre_tflops / PEAK_FP16_TFLOPS, 4),
+            "traffic": measured_traffic(traffic_key, pre_kernel),
             "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
             "algorithmic_bytes": pcfg_bytes,
-            "launch_ms": round(pre_ms, 5),
+            "launch_ms": pre_st,
         },
         "decode": {
             "metric": "paged-decode KV GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
-            "launch_ms": round(dec_ms, 5),
+            "value_from": "median call duration (split + merge) over the timed steps",
+            "launch_ms": dec_st,
+            "split_kernel_us_profile": split_us, "merge_kernel_us_profile": merge_us,
+            "split_merge_source": "profiles/kernel_stats_" + traffic_key + ".md (rocprofv3 kernel-trace averages)",
             "roofline": {
                 "bound": "hbm", "kernel": "decode_split_kernel<2> + decode_merge_kernel",
-                "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                "achieved": round(dec_gbs_mean, 1), "achieved_from": "mean call duration",
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs_mean / PEAK_HBM_GBS, 4),
                 "traffic": measured_traffic(traffic_key, "decode_split_kernel"),
             },
         },
+        "pages_method": pm,
     }
     line["kv_append"] = time_kv_append(pcfg, k, v, dev, stream, W, traffic_key)
     line["qk_norm_rope_append"] = time_qk_norm_rope(pcfg, q, k, v, dev, stream, W, traffic_key,
