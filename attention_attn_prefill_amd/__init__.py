@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     attn_cross_attention,
     attn_cross_attention_workspace_size,
     attn_decode_paged,
+    attn_decode_paged_scratch,
     attn_decode_paged_shared_prefix,
     attn_decode_paged_shared_prefix_workspace_size,
     attn_decode_paged_workspace_size,

@@ -51,6 +51,8 @@ def load_library():
     lib.attn_decode_paged_workspace_size.restype = SZ
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I64, P, SZ, P]
     lib.attn_decode_paged.restype = I
+    lib.attn_decode_paged_scratch.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I64, P]
+    lib.attn_decode_paged_scratch.restype = I
     lib.attn_kv_append.argtypes = [P, P, P, P, P, I64, I, I, I, I64, P]
     lib.attn_kv_append.restype = I
     lib.attn_rope_table.argtypes = [P, P, I, I, D_, P]
@@ -164,6 +166,19 @@ def attn_decode_paged(q, k_cache, v_cache, out, block_tables, seq_lens, workspac
     (single pass).
     """
     import torch
+    if workspace is None:
+        ws, ws_bytes = ctypes.c_void_p(None), 0
+    else:
+        ws = _dev_tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    st = load_library().attn_decode_paged(*_decode_args(q, k_cache, v_cache, out, block_tables, seq_lens),
+                                          ws, ws_bytes, _stream_handle(stream, q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_paged")
+
+
+def _decode_args(q, k_cache, v_cache, out, block_tables, seq_lens):
+    import torch
     num_seqs, H_q, D = q.shape
     num_blocks, H_kv, block_size, Dk = k_cache.shape
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
@@ -173,18 +188,22 @@ def attn_decode_paged(q, k_cache, v_cache, out, block_tables, seq_lens, workspac
         raise ValueError("block_tables / seq_lens shape mismatch")
     ptrs = [_dev_tensor(x, torch.float16, n) for x, n in
             ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out"))]
-    bt = _dev_tensor(block_tables, torch.int32, "block_tables")
-    sl = _dev_tensor(seq_lens, torch.int32, "seq_lens")
-    if workspace is None:
-        ws, ws_bytes = ctypes.c_void_p(None), 0
-    else:
-        ws = _dev_tensor(workspace, torch.uint8, "workspace")
-        ws_bytes = workspace.numel()
-    st = load_library().attn_decode_paged(*ptrs, bt, sl, num_seqs, H_q, H_kv, D,
-                                          block_tables.shape[1], block_size, num_blocks,
-                                          ws, ws_bytes, _stream_handle(stream, q.device))
+    ptrs.append(_dev_tensor(block_tables, torch.int32, "block_tables"))
+    ptrs.append(_dev_tensor(seq_lens, torch.int32, "seq_lens"))
+    return ptrs + [num_seqs, H_q, H_kv, D, block_tables.shape[1], block_size, num_blocks]
+
+
+def attn_decode_paged_scratch(q, k_cache, v_cache, out, block_tables, seq_lens, stream=None) -> None:
+    """Split-K paged decode via ``attn_decode_paged_scratch``: the arguments of
+    ``attn_decode_paged`` without a workspace; the partials go to the
+    library's own per-device array (ATTN_DECODE_SCRATCH_BYTES), so the call
+    allocates nothing.  Calls that overlap on one device race on that array."""
+    import torch
+    args = _decode_args(q, k_cache, v_cache, out, block_tables, seq_lens)
+    with torch.cuda.device(q.device):  # the library uses the current device's array
+        st = load_library().attn_decode_paged_scratch(*args, _stream_handle(stream, q.device))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_decode_paged")
+        raise AttnError(st, "attn_decode_paged_scratch")
 
 
 def attn_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:

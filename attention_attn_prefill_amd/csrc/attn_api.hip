@@ -1,9 +1,12 @@
 // attn_api.hip -- the extern "C" entry points of libattn.so (see
 // include/attn.h): host-side argument validation, then kernel launches on the
-// caller's stream.  No allocation, no synchronisation, no global state.
+// caller's stream.  No allocation and no synchronisation; the only global
+// state is the per-device address of attn_decode_paged_scratch's array.
 #include "../../include/attn.h"
 
 #include <math.h>
+
+#include <mutex>
 
 #include "attn_internal.h"
 
@@ -140,28 +143,20 @@ ATTN_EXPORT size_t attn_decode_paged_workspace_size(int num_seqs, int H_q, int H
   return plan_decode(num_seqs, H_q, H_kv, max_blocks_per_seq).ws_bytes;
 }
 
-ATTN_EXPORT attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                                            void* out, const int32_t* block_tables,
-                                            const int32_t* seq_lens, int num_seqs, int H_q,
-                                            int H_kv, int head_dim, int max_blocks_per_seq,
-                                            int block_size, int64_t num_blocks, void* workspace,
-                                            size_t workspace_bytes, void* stream) {
-  if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens) return ATTN_ERR_INVALID_ARG;
-  const attn_status_t st =
-      check_decode_shape(num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size);
-  if (st != ATTN_OK) return st;
-  if (num_blocks <= 0) return ATTN_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
-    return ATTN_ERR_INVALID_ARG;
-  if (workspace && !aligned(workspace, 16)) return ATTN_ERR_INVALID_ARG;
-
+// Validation, planning and launch of plain paged decode.  `ws` (may be null)
+// holds `ws_bytes` bytes; null means the single-pass path, one split per
+// (sequence, kv head).
+static attn_status_t decode_paged(const void* q, const void* k_cache, const void* v_cache, void* out,
+                                  const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                                  int H_q, int H_kv, int head_dim, int max_blocks_per_seq,
+                                  int block_size, int64_t num_blocks, float* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   DecodePlan plan = plan_decode(num_seqs, H_q, H_kv, max_blocks_per_seq);
-  if (workspace == nullptr || plan.ws_bytes == 0) {
+  if (ws == nullptr || plan.ws_bytes == 0) {
     // single pass: one split covers the whole table width
     plan.split_blocks = max_blocks_per_seq;
     plan.n_split_max = 1;
-  } else if (workspace_bytes < plan.ws_bytes) {
+  } else if (ws_bytes < plan.ws_bytes) {
     return ATTN_ERR_WORKSPACE;
   }
   if ((int64_t)plan.n_split_max * H_kv * num_seqs > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
@@ -173,7 +168,6 @@ ATTN_EXPORT attn_status_t attn_decode_paged(const void* q, const void* k_cache, 
   a.out = static_cast<_Float16*>(out);
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
-  float* ws = static_cast<float*>(workspace);
   const int64_t slots = (int64_t)num_seqs * H_q * plan.n_split_max;
   a.ws_o = plan.n_split_max > 1 ? ws : nullptr;
   a.ws_ml = plan.n_split_max > 1 ? ws + slots * attn::kDecodeHeadDim : nullptr;
@@ -192,8 +186,102 @@ ATTN_EXPORT attn_status_t attn_decode_paged(const void* q, const void* k_cache, 
   a.max_group_size = 0;
   a.prefix_slots = 0;
   a.slot_stride = plan.n_split_max;
-  const hipError_t e = attn::launch_decode(a, H_q / H_kv, static_cast<hipStream_t>(stream));
+  const hipError_t e = attn::launch_decode(a, H_q / H_kv, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+static attn_status_t check_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                                       const void* out, const int32_t* block_tables,
+                                       const int32_t* seq_lens, int num_seqs, int H_q, int H_kv,
+                                       int head_dim, int max_blocks_per_seq, int block_size,
+                                       int64_t num_blocks) {
+  if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens) return ATTN_ERR_INVALID_ARG;
+  const attn_status_t st =
+      check_decode_shape(num_seqs, H_q, H_kv, head_dim, max_blocks_per_seq, block_size);
+  if (st != ATTN_OK) return st;
+  if (num_blocks <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+ATTN_EXPORT attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                            void* out, const int32_t* block_tables,
+                                            const int32_t* seq_lens, int num_seqs, int H_q,
+                                            int H_kv, int head_dim, int max_blocks_per_seq,
+                                            int block_size, int64_t num_blocks, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  const attn_status_t st = check_decode_args(q, k_cache, v_cache, out, block_tables, seq_lens, num_seqs,
+                                             H_q, H_kv, head_dim, max_blocks_per_seq, block_size,
+                                             num_blocks);
+  if (st != ATTN_OK) return st;
+  if (workspace && !aligned(workspace, 16)) return ATTN_ERR_INVALID_ARG;
+  return decode_paged(q, k_cache, v_cache, out, block_tables, seq_lens, num_seqs, H_q, H_kv, head_dim,
+                      max_blocks_per_seq, block_size, num_blocks, static_cast<float*>(workspace),
+                      workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---- paged decode without allocation ---------------------------------------
+// The split-K partials go to a library-owned array in device memory instead of
+// a caller workspace.  Each device holds its own copy from the library's load
+// until the process ends; its address differs per device and is looked up
+// (with that device current) on the first call there.  Nothing in it needs
+// clearing: the merge reads only the partial slots that the same call's split
+// kernel wrote.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)ATTN_DECODE_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices];  // per device, set once under the mutex
+
+// Device address of `scratch` on device `dev` (current).  Null on failure.
+float* scratch_on(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+ATTN_EXPORT attn_status_t attn_decode_paged_scratch(const void* q, const void* k_cache,
+                                                    const void* v_cache, void* out,
+                                                    const int32_t* block_tables,
+                                                    const int32_t* seq_lens, int num_seqs, int H_q,
+                                                    int H_kv, int head_dim, int max_blocks_per_seq,
+                                                    int block_size, int64_t num_blocks, void* stream) {
+  const attn_status_t st = check_decode_args(q, k_cache, v_cache, out, block_tables, seq_lens, num_seqs,
+                                             H_q, H_kv, head_dim, max_blocks_per_seq, block_size,
+                                             num_blocks);
+  if (st != ATTN_OK) return st;
+  const DecodePlan plan = plan_decode(num_seqs, H_q, H_kv, max_blocks_per_seq);
+  if (plan.ws_bytes > kScratchBytes) return ATTN_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+    if (s != nullptr) {
+      // the scratch looked up below is the current device's: the stream must
+      // belong to it
+      hipDevice_t sdev = -1;
+      if (hipStreamGetDevice(s, &sdev) != hipSuccess) return ATTN_ERR_LAUNCH;
+      if (sdev != dev) return ATTN_ERR_INVALID_ARG;
+    }
+    ws = scratch_on(dev);
+    if (ws == nullptr) return ATTN_ERR_LAUNCH;
+  }
+  return decode_paged(q, k_cache, v_cache, out, block_tables, seq_lens, num_seqs, H_q, H_kv, head_dim,
+                      max_blocks_per_seq, block_size, num_blocks, ws, kScratchBytes, s);
 }
 
 // ---- shared-prefix (forked) paged decode ----------------------------------

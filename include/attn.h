@@ -18,7 +18,9 @@
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers (HIP device memory or memory the device can
  *     address), except where stated.  The caller owns every buffer; the library
- *     allocates nothing, keeps no state between calls and is reentrant.
+ *     allocates nothing, keeps no state between calls and is reentrant, with
+ *     one exception: attn_decode_paged_scratch uses a fixed array of its own
+ *     in device memory (see there).
  *   - fp16 tensors are IEEE binary16, dense, row-major, with the layouts given
  *     below; every fp16 base pointer must be 16-byte aligned, int32 pointers
  *     4-byte aligned.
@@ -47,7 +49,9 @@ typedef enum attn_status_t {
                                causal with S_q != S_kv, misaligned pointer */
   ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, block_size,
                                H_q / H_kv ratio outside the supported set */
-  ATTN_ERR_WORKSPACE = 3,   /* workspace non-NULL but smaller than required */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace non-NULL but smaller than required,
+                               or more than attn_decode_paged_scratch's
+                               fixed array holds */
   ATTN_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch */
 } attn_status_t;
 
@@ -130,6 +134,44 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache,
                                 int block_size, int64_t num_blocks,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * Size in bytes of the device array behind attn_decode_paged_scratch (one
+ * copy per device).
+ */
+#define ATTN_DECODE_SCRATCH_BYTES (16u << 20)
+
+/*
+ * Paged decode that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory around the call: code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, layouts, preconditions and result are those of
+ * attn_decode_paged given a workspace of
+ * attn_decode_paged_workspace_size(...) bytes (split-K decoding; the same
+ * kernels run).  The split-K partials live instead in an array of
+ * ATTN_DECODE_SCRATCH_BYTES bytes that the library holds in the memory of
+ * each device it runs on until the process ends.
+ *
+ *   - A call whose workspace size exceeds ATTN_DECODE_SCRATCH_BYTES returns
+ *     ATTN_ERR_WORKSPACE and enqueues nothing (e.g. H_q = 16 allows 64
+ *     sequences of 32768 tokens; use attn_decode_paged for more).
+ *   - The array of the CURRENT device is used; a non-NULL stream must belong
+ *     to that device (else ATTN_ERR_INVALID_ARG).  Its device address is
+ *     looked up on the first call on each device (under a lock), so make one
+ *     call on a device before capturing a graph there.
+ *   - Every call on a device shares that device's array.  Calls whose work
+ *     overlaps on one device (other streams, other host threads, concurrent
+ *     graph replays) race on it and give wrong results: order them.
+ *     Sequential calls need no clearing between them; each call rewrites
+ *     every part of the array that it reads.
+ */
+attn_status_t attn_decode_paged_scratch(const void* q, const void* k_cache,
+                                        const void* v_cache, void* out,
+                                        const int32_t* block_tables,
+                                        const int32_t* seq_lens, int num_seqs,
+                                        int H_q, int H_kv, int head_dim,
+                                        int max_blocks_per_seq, int block_size,
+                                        int64_t num_blocks, void* stream);
 
 /*
  * Bytes of device workspace attn_decode_paged_shared_prefix needs; 0 for

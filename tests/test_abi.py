@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "attn_abi_version", "attn_status_string", "attn_prefill", "attn_prefill_qk_norm_rope",
-        "attn_decode_paged_workspace_size", "attn_decode_paged", "attn_kv_append",
+        "attn_decode_paged_workspace_size", "attn_decode_paged", "attn_decode_paged_scratch",
+        "attn_kv_append",
         "attn_rope_table", "attn_qk_norm_rope", "attn_qk_norm_rope_append",
         "attn_cross_attention_workspace_size", "attn_cross_attention",
         "attn_decode_paged_shared_prefix_workspace_size", "attn_decode_paged_shared_prefix"])
@@ -98,6 +99,24 @@ def decode(lib, q=P, kc=P, vc=P, out=P2, bt=P, sl=P, num_seqs=4, H_q=16, H_kv=8,
 ])
 def test_decode_rejects(lib, kw, want):
     assert decode(lib, **kw) == want
+
+
+def decode_scratch(lib, q=P, kc=P, vc=P, out=P2, bt=P, sl=P, num_seqs=4, H_q=16, H_kv=8, D=128,
+                   max_bps=256, bs=16, num_blocks=100):
+    return lib.attn_decode_paged_scratch(q, kc, vc, out, bt, sl, num_seqs, H_q, H_kv, D, max_bps,
+                                         bs, num_blocks, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), INV), (dict(out=NULL), INV), (dict(sl=NULL), INV), (dict(num_seqs=0), INV),
+    (dict(H_q=12, H_kv=8), INV), (dict(num_blocks=0), INV), (dict(D=64), UNS), (dict(bs=32), UNS),
+    (dict(bt=ctypes.c_void_p(0x10002)), INV),
+    # 64 sequences, 4096-block tables, H_q = 16: 16.25 MiB of partials, more
+    # than the library's 16 MiB array
+    (dict(num_seqs=64, max_bps=4096), WS), (dict(num_seqs=128, max_bps=2048), WS),
+])
+def test_decode_scratch_rejects(lib, kw, want):
+    assert decode_scratch(lib, **kw) == want
 
 
 def test_workspace_size(lib):
