@@ -36,25 +36,56 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    objdir = os.path.join(ROOT, "_build")
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the argument
+# validation in attn_api.hip (device code is built as usual).  A process that
+# loads such a build needs clang's ASan runtime preloaded (asan_runtime()).
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=all",
+                       "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime():
+    """Path of the ROCm clang ASan runtime matching HOST_SANITIZE_FLAGS, or None."""
+    out = subprocess.run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = out.stdout.strip().splitlines()[-1] if out.returncode == 0 and out.stdout.strip() else ""
+    if os.path.isabs(path) and os.path.exists(path):
+        return path
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return found[-1] if found else None
+
+
+def build(verbose: bool = False, extra_flags=(), host_sanitize: bool = False, out: str = None,
+          jobs: int = 1) -> str:
+    """Compile every source and link libattn.so (or `out`).  `host_sanitize`
+    builds the host code with HOST_SANITIZE_FLAGS into a separate object dir."""
+    lib = out or LIB
+    objdir = os.path.join(ROOT, "_build", "host_sanitize" if host_sanitize else "")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         cmd = [HIPCC, *FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), *extra_flags,
-               "-c", "-o", obj, src]
+               *(HOST_SANITIZE_FLAGS if host_sanitize else []), "-c", "-o", obj, src]
         cmd.remove("-shared")
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        cmds.append(cmd)
         objs.append(obj)
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+    for i in range(0, len(cmds), max(1, jobs)):
+        procs = []
+        for cmd in cmds[i:i + max(1, jobs)]:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append(subprocess.Popen(cmd))
+        if any(p.wait() != 0 for p in procs):
+            raise subprocess.CalledProcessError(1, "hipcc")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp", *objs]
+    if host_sanitize:
+        cmd += ["-Xarch_host", "-fsanitize=address,undefined", "-shared-libsan"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

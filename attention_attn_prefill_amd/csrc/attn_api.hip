@@ -66,6 +66,7 @@ ATTN_EXPORT const char* attn_status_string(attn_status_t status) {
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
+    case ATTN_STATUS_MAX_ENUM: break;
   }
   return "ATTN_ERR_UNKNOWN";
 }

@@ -52,13 +52,18 @@ typedef enum attn_status_t {
   ATTN_ERR_WORKSPACE = 3,   /* workspace non-NULL but smaller than required,
                                or more than attn_decode_paged_scratch's
                                fixed array holds */
-  ATTN_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch */
+  ATTN_ERR_LAUNCH = 4,      /* the HIP runtime refused a kernel launch */
+  ATTN_STATUS_MAX_ENUM = 0x7fffffff /* never returned: makes every int from 0
+                                       to INT_MAX a valid attn_status_t, so
+                                       attn_status_string may be passed any
+                                       such code */
 } attn_status_t;
 
 /* Version of this ABI; bumped on any incompatible change. */
 int attn_abi_version(void);
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Human-readable name of a status code (static string, never NULL;
+   "ATTN_ERR_UNKNOWN" for a value that is no status). */
 const char* attn_status_string(attn_status_t status);
 
 /*

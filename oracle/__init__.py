@@ -44,10 +44,11 @@ class Oracle:
             return self._lib
         path = self._path
         if path is None:
-            path = _build.LIB
+            sanitize = _build.sanitize_requested()
+            path = _build.LIB_SAN if sanitize else _build.LIB
             src_mtime = os.path.getmtime(_build.SRC)
             if not os.path.exists(path) or os.path.getmtime(path) < src_mtime:
-                _build.build()
+                _build.build(sanitize=sanitize)
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int

@@ -74,8 +74,8 @@ def test_mutant_is_caught(tmp_path, desc, old, new):
     path_c = tmp_path / "mutant.c"
     path_c.write_text(src.replace(old, new))
     lib = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", str(lib),
-                    str(path_c), "-lm"], check=True)
+    flags = obuild.cflags(sanitize=obuild.sanitize_requested(), opt="-O1")
+    subprocess.run(["gcc"] + flags + ["-w", "-o", str(lib), str(path_c), "-lm"], check=True)
     ora = oracle.Oracle(str(lib))
     failed = []
     for pin in ALL_PINS:
