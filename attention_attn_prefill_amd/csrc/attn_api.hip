@@ -506,10 +506,15 @@ static attn_status_t check_cross(int B, int T_q, int T_k, int dim, int H) {
   const int D = dim / H;
   if (D != 32 && D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (dim % 32) return ATTN_ERR_UNSUPPORTED;
-  // every operand below 2 GiB (32-bit buffer offsets), also per batch entry for attention
+  // 32-bit byte offsets: the projections address whole 32-row tiles of every
+  // operand, and the attention step (the prefill rules) whole 64-key tiles
+  // of one batch entry's K/V plus three tiles of staging margin
   const int64_t rows = (int64_t)B * (T_q > T_k ? T_q : T_k);
-  if (rows * dim * 2 >= ((int64_t)1 << 31) || (int64_t)dim * dim * 2 >= ((int64_t)1 << 31))
+  if (ceil_div64(rows, 32) * 32 * dim * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)dim * dim * 2 >= ((int64_t)1 << 31))
     return ATTN_ERR_UNSUPPORTED;
+  if ((ceil_div64(T_k, 64) + 3) * 64 * dim * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (ceil_div64(T_q, 128) * H * B > (int64_t)0x7fffffff) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 

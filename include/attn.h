@@ -386,7 +386,11 @@ size_t attn_cross_attention_workspace_size(int B, int T_q, int T_k, int dim, int
  * to fp16 in between (the MFMA operand precision).  workspace: at least
  * attn_cross_attention_workspace_size(...) bytes, 256-byte aligned (NULL or
  * smaller is ATTN_ERR_WORKSPACE).  D must be 32, 64 or 128, dim a multiple
- * of 32, max_pos >= max(T_q, T_k).
+ * of 32, max_pos >= max(T_q, T_k).  32-bit byte offsets bound the sizes
+ * (larger is ATTN_ERR_UNSUPPORTED): ceil(B * max(T_q, T_k) / 32) * 32 * dim
+ * * 2 < 2^31 (the projections address whole 32-row tiles), dim * dim * 2 <
+ * 2^31, and (ceil(T_k / 64) + 3) * 64 * dim * 2 < 2^31 (the attention step,
+ * as for attn_prefill).
  */
 attn_status_t attn_cross_attention(const void* x_q, const void* x_kv, const void* w_q,
                                    const void* w_k, const void* w_v, const void* w_o,

@@ -257,6 +257,18 @@ def test_cross_attention_workspace_size(lib):
     assert lib.attn_cross_attention_workspace_size(4, 64, 128, 256, 16) == 0
 
 
+def test_cross_attention_32bit_offset_limits(lib):
+    f = lib.attn_cross_attention_workspace_size
+    # dim 1024: the projections address whole 32-row tiles, so 2^20 - 32 rows
+    # fit 32-bit byte offsets and 2^20 - 1 rows (rounded up to 2^20) do not
+    assert f(1, (1 << 20) - 32, 64, 1024, 8) > 0
+    assert f(1, (1 << 20) - 1, 64, 1024, 8) == 0
+    # the attention step: whole 64-key tiles of one batch entry plus three,
+    # (ceil(T_k / 64) + 3) * 64 * 1024 * 2 < 2^31, so T_k <= 16380 * 64
+    assert f(1, 64, 16380 * 64, 1024, 8) > 0
+    assert f(1, 64, 16380 * 64 + 1, 1024, 8) == 0
+
+
 def shared(lib, q=P, kc=P, vc=P, out=P2, bt=P, sl=P, num_seqs=256, H_q=16, H_kv=8, D=128, mbs=160, bs=16,
            nb=9000, gs=P, pb=P, ng=32, mgs=8, ws=ctypes.c_void_p(0x40000), wsb=1 << 30):
     return lib.attn_decode_paged_shared_prefix(q, kc, vc, out, bt, sl, num_seqs, H_q, H_kv, D, mbs, bs, nb, gs,
