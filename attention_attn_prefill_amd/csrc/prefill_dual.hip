@@ -329,10 +329,15 @@ struct Dual {
         // keep the add in this chunk (otherwise it sinks to the loop latch)
         asm volatile("" : "+v"(ls[g][(r >> 1) & 1]));
       }
-      // the reads of chunk i + AHEAD: a K k-step on even chunks, a V half on every chunk
+      // the reads of chunk i + AHEAD, on even chunks only: a K k-step, or
+      // both halves of a V operand (LDS reads cost least next to MFMAs in the
+      // chunks without the fp16 packing and the row-sum adds)
       const int n = i + AHEAD;
       if (n < 16 && !(n & 1)) read_k(n >> 1);
-      if (n >= 16 - 2 && n < 32 - 2) read_v(n - 14);
+      if (n >= 16 - 2 && n < 32 - 2 && !(n & 1)) {
+        read_v(n - 14);
+        read_v(n - 13);
+      }
       if (STAGE && i < COPIES) copy(i, t + 2, t + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
