@@ -43,6 +43,12 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, _Flo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, offset, 0, 0, 0);
 }
 
+// The same with the LDS destination given as a byte address in LDS (uniform).
+__device__ __forceinline__ void buffer_load16_lds_at(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, int offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds_addr, 16, offset, 0,
+                                           0, 0);
+}
+
 // s_waitcnt vmcnt(0): every buffer load of this wavefront, the copies into
 // LDS among them, has landed (lgkmcnt and expcnt left at their maximum)
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -115,6 +115,10 @@ struct Dual {
   // wavefront copies: row * row_bytes + 16 * chunk, or kPadOffset where the
   // block position is row padding (an out-of-range load writes zeros there)
   uint32_t k_off[K_COPIES], v_off[V_COPIES];
+  // LDS byte address of the block each copy fills, per slot (the spare block
+  // for a dummy copy); uniform, so they live in SGPRs and a copy costs one
+  // scalar select into M0
+  uint32_t k_dst[2][K_COPIES], v_dst[2][V_COPIES];
   int S_kv;
   int mask_from;  // first sub-block that may need the element mask
   int n_tiles;    // K/V tiles the workgroup stages
@@ -145,19 +149,32 @@ struct Dual {
       off[j] = c < VEC_ROW ? (uint32_t)r * row_bytes + 16u * c : kPadOffset;
     }
   }
-  __device__ __forceinline__ _Float16* copy_dst(_Float16* slot, int blocks, int j) const {
-    const int i = wave + kWaves * j;
-    return i < blocks ? slot + i * 512 : smem + LDS_HALFS;  // spare block past the tiles
+  __device__ __forceinline__ void copy_dsts() {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) _Float16*)smem;
+    const uint32_t spare = lds0 + LDS_HALFS * 2;  // the spare block past the tiles
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+      for (int j = 0; j < K_COPIES; ++j) {
+        const int i = wave + kWaves * j;
+        k_dst[sl][j] = i < K_BLOCKS ? lds0 + (sl * K_LDS + i * 512) * 2 : spare;
+      }
+#pragma unroll
+      for (int j = 0; j < V_COPIES; ++j) {
+        const int i = wave + kWaves * j;
+        v_dst[sl][j] = i < V_BLOCKS ? lds0 + (2 * K_LDS + sl * V_LDS + i * 512) * 2 : spare;
+      }
+    }
   }
   // copy n of the tile pair (K tile tk, V tile tv); n < COPIES
   __device__ __forceinline__ void copy(int n, int tk, int tv) {
     if (n < K_COPIES) {
-      dev::buffer_load16_lds(krsrc, copy_dst(smem + (tk & 1) * K_LDS, K_BLOCKS, n),
-                             (int)(k_off[n] + (uint32_t)tk * kTile * row_bytes));
+      const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)tk * kTile * row_bytes);
+      dev::buffer_load16_lds_at(krsrc, (tk & 1) ? k_dst[1][n] : k_dst[0][n], (int)(k_off[n] + base));
     } else {
       const int j = n - K_COPIES;
-      dev::buffer_load16_lds(vrsrc, copy_dst(smem + 2 * K_LDS + (tv & 1) * V_LDS, V_BLOCKS, j),
-                             (int)(v_off[j] + (uint32_t)tv * kTile * row_bytes));
+      const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)tv * kTile * row_bytes);
+      dev::buffer_load16_lds_at(vrsrc, (tv & 1) ? v_dst[1][j] : v_dst[0][j], (int)(v_off[j] + base));
     }
   }
   __device__ __forceinline__ void copy_tiles(int tk, int tv) {
@@ -599,6 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
   w.vrsrc = dev::make_rsrc(vbase, range);
   w.template copy_offsets<W::KROW>(w.k_off, W::K_COPIES);
   w.template copy_offsets<W::VROW>(w.v_off, W::V_COPIES);
+  w.copy_dsts();
 
   w.setup(a, hi, hg);
   w.issue_tile_loads(a);
