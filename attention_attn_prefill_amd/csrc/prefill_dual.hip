@@ -293,8 +293,10 @@ struct Dual {
   }
 
   // Step u (parity PAR) of the loop: S(u+1) = K Q^T into s[PAR ^ 1], the
-  // softmax of s[PAR] into p[PAR], and O += V^T P(u-1)^T; with STAGE the
-  // iteration's tile staging goes into the same step.
+  // softmax of s[PAR] into p[PAR], and O += V^T P(u-1)^T.  STAGE 1 issues
+  // the iteration's K tile copies in the first chunks of the step, STAGE 2
+  // its V tile copies (one half of the staging in each step of an iteration
+  // costs less issue time than all of it in one).
   //
   // The three parts are independent, and a wavefront is alone on its SIMD,
   // so the instruction order is spelled out: 32 chunks, each one MFMA (16 of
@@ -303,7 +305,7 @@ struct Dual {
   // of two earlier elements, and the LDS operand reads about six MFMAs
   // before their use.  A scheduling fence after every chunk keeps the
   // compiler from regrouping MFMAs and VALU work into runs.
-  template <int PAR, bool MASK, bool STAGE>
+  template <int PAR, bool MASK, int STAGE>
   __device__ __forceinline__ void step(int u, int t) {
     constexpr int PP = PAR ^ 1;
     constexpr int AHEAD = 6;  // chunks between an operand read and its MFMA
@@ -355,7 +357,8 @@ struct Dual {
         read_v(n - 14);
         read_v(n - 13);
       }
-      if (STAGE && i < COPIES) copy(i, t + 2, t + 1);
+      if (STAGE == 1 && i < K_COPIES) copy(i, t + 2, t + 1);
+      if (STAGE == 2 && i < V_COPIES) copy(K_COPIES + i, t + 2, t + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     y[31] = __builtin_amdgcn_exp2f(x[31]);
@@ -420,14 +423,14 @@ struct Dual {
     // every key under it).
     int t = 0;
     for (; t < n_tiles && 2 * t + 2 < mask_from; ++t) {
-      step<1, false, true>(2 * t + 1, t);
-      step<0, false, false>(2 * t + 2, t);
+      step<1, false, 1>(2 * t + 1, t);
+      step<0, false, 2>(2 * t + 2, t);
       dev::wait_vmcnt0();
       dev::lds_barrier();
     }
     for (; t < n_tiles; ++t) {
-      step<1, true, true>(2 * t + 1, t);
-      step<0, true, false>(2 * t + 2, t);
+      step<1, true, 1>(2 * t + 1, t);
+      step<0, true, 2>(2 * t + 2, t);
       dev::wait_vmcnt0();
       dev::lds_barrier();
     }
