@@ -32,6 +32,19 @@
  *   - The softmax scale is 1/sqrt(head_dim) (the launch wrappers of the
  *     attention.cu listing), applied to fp32 dot products; accumulation is
  *     fp32; outputs are rounded to fp16 with round-to-nearest-even.
+ *
+ * Where this ABI is its own design rather than the pages':
+ *   - attn_abi_version, attn_status_string, the status codes and the
+ *     *_workspace_size queries have no counterpart on the pages (whose
+ *     launchers return nothing and abort on a CUDA error);
+ *   - `stream` is a void* carrying a hipStream_t, so that this header needs
+ *     no HIP include; the pages' launch wrappers take the runtime's stream
+ *     type;
+ *   - attn_decode_paged takes num_blocks (to bound every table entry) and a
+ *     caller workspace for split-K decoding, which the pages' decode
+ *     signature does not have;
+ *   - attn_prefill takes S_q, S_kv and `causal` where the pages have one S
+ *     and always mask.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
