@@ -305,10 +305,18 @@ struct Dual {
   // of two earlier elements, and the LDS operand reads about six MFMAs
   // before their use.  A scheduling fence after every chunk keeps the
   // compiler from regrouping MFMAs and VALU work into runs.
-  template <int PAR, bool MASK, int STAGE>
-  __device__ __forceinline__ void step(int u, int t) {
+  // The first K operands of a step are read AHEAD / 2 = 3 k-steps ahead of
+  // its first MFMA.  The second step of an iteration reads the same K tile
+  // as the first, already resident, so the first step reads them for it in
+  // its last chunks (PRE_OUT, into kpre) and the second step starts on them
+  // (PRE_IN) instead of waiting on fresh LDS reads.  The first step's K tile
+  // only becomes visible at the iteration's barrier.
+  static constexpr int PRE = 3;
+  template <int PAR, bool MASK, int STAGE, bool PRE_IN, bool PRE_OUT>
+  __device__ __forceinline__ void step(int u, int t, half8_t (&kpre)[PRE]) {
     constexpr int PP = PAR ^ 1;
     constexpr int AHEAD = 6;  // chunks between an operand read and its MFMA
+    static_assert(AHEAD == 2 * PRE, "the prefetched K operands are the up-front ones");
 #pragma unroll
     for (int g = 0; g < 2; ++g) l[g] += lsum[g];
     if (MASK) mask<PAR>(u);
@@ -327,7 +335,12 @@ struct Dual {
       vr[v] = dev::lds_read_tr(vl + (16 * cc + 8 * (v & 1)) * VROW + dt * 32);
     };
 #pragma unroll
-    for (int ks = 0; 2 * ks < AHEAD; ++ks) read_k(ks);
+    for (int ks = 0; 2 * ks < AHEAD; ++ks) {
+      if (PRE_IN) kf[ks] = kpre[ks];
+      else read_k(ks);
+    }
+    // the next step's K sub-block (u + 2, parity PAR), for PRE_OUT
+    const _Float16* kb_next = smem + (((u + 2) >> 1) & 1) * K_LDS + k_lane + PAR * 32 * KROW;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -356,6 +369,10 @@ struct Dual {
       if (n >= 16 - 2 && n < 32 - 2 && !(n & 1)) {
         read_v(n - 14);
         read_v(n - 13);
+      }
+      if (PRE_OUT && i >= 32 - PRE - 2 && i < 32 - 2) {
+        const int ks = i - (32 - PRE - 2);
+        kpre[ks] = *reinterpret_cast<const half8_t*>(kb_next + 16 * ks);
       }
       if (STAGE == 1 && i < K_COPIES) copy(i, t + 2, t + 1);
       if (STAGE == 2 && i < V_COPIES) copy(K_COPIES + i, t + 2, t + 1);
@@ -422,15 +439,16 @@ struct Dual {
     // the rest with the element mask on (a sub-block that needs no mask keeps
     // every key under it).
     int t = 0;
+    half8_t kpre[PRE];
     for (; t < n_tiles && 2 * t + 2 < mask_from; ++t) {
-      step<1, false, 1>(2 * t + 1, t);
-      step<0, false, 2>(2 * t + 2, t);
+      step<1, false, 1, false, true>(2 * t + 1, t, kpre);
+      step<0, false, 2, true, false>(2 * t + 2, t, kpre);
       dev::wait_vmcnt0();
       dev::lds_barrier();
     }
     for (; t < n_tiles; ++t) {
-      step<1, true, 1>(2 * t + 1, t);
-      step<0, true, 2>(2 * t + 2, t);
+      step<1, true, 1, false, true>(2 * t + 1, t, kpre);
+      step<0, true, 2, true, false>(2 * t + 2, t, kpre);
       dev::wait_vmcnt0();
       dev::lds_barrier();
     }
