@@ -71,6 +71,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier with no memory fence, for points where each wavefront
+// has already waited for what the others will read (its copies into LDS by
+// vmcnt, its LDS reads by using their results).  A fenced barrier would also
+// wait for every store and load still in flight (copies into LDS count on
+// vmcnt, so the memory model makes a fence on LDS wait for all of them).
+// The empty asm keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void plain_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // 4 fp16 values through the transposing LDS read: in each 16-lane group,
 // lanes 4j..4j+3 read 16 consecutive halfs of row j and lane i receives
 // column i of rows 0..3.

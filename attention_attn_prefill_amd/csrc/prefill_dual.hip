@@ -99,13 +99,14 @@ struct Dual {
   static constexpr int COPIES = K_COPIES + V_COPIES;
   static constexpr int ROWS_WG = HP == 2 ? 4 * 32 : 4 * 64;  // query rows per head and workgroup
   static constexpr int OROW = D + 8;                         // LDS row stride of the output tiles
-  static constexpr int OUT_LDS = 8 * 32 * OROW;               // output tiles, after the K/V slots and the spare block
-  static constexpr int SMEM_HALFS = LDS_HALFS + 512 + OUT_LDS;
+  static constexpr int OUT_LDS = 8 * 32 * OROW;               // output tiles (an LDS array of their own)
+  static constexpr int SMEM_HALFS = LDS_HALFS + 512;            // the K/V slots and the spare block
   static_assert(K_BLOCKS * 1024 == kTile * KROW * 2 && V_BLOCKS * 1024 == kTile * VROW * 2,
                 "tiles must be whole 1 KB blocks");
-  static_assert(SMEM_HALFS * 2 <= 160 * 1024, "LDS of one workgroup");
+  static_assert((SMEM_HALFS + OUT_LDS) * 2 <= 160 * 1024, "LDS of one workgroup");
 
-  _Float16* smem;
+  _Float16* smem;   // the K/V slots and the spare block
+  _Float16* osmem;  // the output tiles of the epilogue
   int tid, lane, hf, col;
   int wave;  // wavefront index in the workgroup (uniform: from readfirstlane)
   int k_lane, v_lane;  // this lane's offsets in a K / V tile (halfs)
@@ -117,7 +118,9 @@ struct Dual {
   uint32_t k_off[K_COPIES], v_off[V_COPIES];
   // LDS byte address of the block each copy fills, per slot (the spare block
   // for a dummy copy); uniform, so they live in SGPRs and a copy costs one
-  // scalar select into M0
+  // scalar select into M0.  Given as integers, the copies carry no pointer
+  // the compiler could relate to the operand reads, so it places no wait for
+  // them before those reads (the iteration's vmcnt(0) and barrier order them)
   uint32_t k_dst[2][K_COPIES], v_dst[2][V_COPIES];
   int S_kv;
   int mask_from;  // first sub-block that may need the element mask
@@ -393,7 +396,7 @@ struct Dual {
   }
 
   // One pass over the keys, with the Q fragments loaded and K(0), V(0),
-  // K(1) in LDS (published by a barrier).  KNOWN_REF: the references mb are
+  // K(1) in LDS (published by the caller's barrier).  KNOWN_REF: the references mb are
   // the exact row maxima; else the first sub-block sets them.
   // Returns true when a row-sum share above kShareMax was seen anywhere in the
   // workgroup (workgroup-uniform).
@@ -413,7 +416,6 @@ struct Dual {
       lsum[g] = 0.0f;
     }
     share_max = 0.0f;
-    dev::lds_barrier();
 
     // first sub-blocks: S(0) and S(1) (both from K(0)) and the softmax of
     // S(0); without known references the exact max of S(0) becomes the
@@ -426,7 +428,10 @@ struct Dual {
       for (int g = 0; g < 2; ++g) mb[g] = half_swap_max(max16(s[0][g])) * c2;
     }
     weights<0>();
-    dev::lds_barrier();  // S(0), S(1) read K(0)'s slot, which iteration 0 overwrites
+    // S(0), S(1) read K(0)'s slot, which iteration 0 overwrites; those reads
+    // have returned (their products are taken), so no fence is needed, and
+    // a fenced barrier would wait for the previous tile's output stores
+    dev::plain_barrier();
 
     // Every wavefront runs every step of the workgroup's key range.  Steps
     // past its own diagonal (or past the keys) are masked to -inf: their
@@ -555,7 +560,7 @@ struct Dual {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const float inv = 1.0f / half_swap_add(l[g]);
-      _Float16* ot = smem + LDS_HALFS + 512 + (wave * 2 + g) * 32 * OROW;
+      _Float16* ot = osmem + (wave * 2 + g) * 32 * OROW;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -567,16 +572,18 @@ struct Dual {
         }
       }
     }
-    // the lanes read rows that other lanes of this wavefront wrote
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    // the lanes read rows that other lanes of this wavefront wrote: a
+    // wavefront's LDS instructions execute in issue order, so only the
+    // compiler must keep the reads after the writes (a fence would also wait
+    // for the next tile's loads, issued before this epilogue)
+    asm volatile("" ::: "memory");
     constexpr int PIECES = D / 8;          // 16-byte pieces per row
     constexpr int ROWS_PER = 64 / PIECES;  // rows per 64-lane store
     const int pr = lane / PIECES, pc = lane % PIECES;
     const bool full = rows0[1] + 31 < a.S_q;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const _Float16* ot = smem + LDS_HALFS + 512 + (wave * 2 + g) * 32 * OROW;
+      const _Float16* ot = osmem + (wave * 2 + g) * 32 * OROW;
 #pragma unroll
       for (int i = 0; i < 32 / ROWS_PER; ++i) {
         const int r = i * ROWS_PER + pr;
@@ -601,6 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
   using W = Dual<CAUSAL, HP>;
   constexpr int D = W::D;
   __shared__ __attribute__((aligned(16))) _Float16 smem[W::SMEM_HALFS];
+  __shared__ __attribute__((aligned(16))) _Float16 osmem[W::OUT_LDS];
   __shared__ int flags[kWaves];
   const int head_groups = a.H_q / HP;
   const int combos = head_groups * a.B;
@@ -615,6 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
 
   W w;
   w.smem = smem;
+  w.osmem = osmem;
   w.tid = (int)__builtin_amdgcn_workitem_id_x();
   w.lane = w.tid & 63;
   // the wavefront index is uniform; readfirstlane lets the compiler see that,
@@ -653,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
     w.issue_tile_loads(a);
     if (w.epilogue(a, rows0, heads)) dev::wait_vmcnt<2 * (D / 8) * 32 / 64>();  // its 16 stores may stay in flight
     else dev::wait_vmcnt0();
-    dev::lds_barrier();
+    dev::plain_barrier();  // every wavefront's copies of the second tile have landed
     w.compute(flags);
   }
   w.epilogue(a, w.row0, w.head);
