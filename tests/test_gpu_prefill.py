@@ -83,6 +83,14 @@ EDGE = [
     # non-causal, S_q != S_kv, two-head workgroups at D = 32 and 64
     (2, 200, 150, 4, 2, 32, False),
     (1, 300, 260, 8, 2, 64, False),
+    # head_dim 128 with an odd H_q / H_kv (one head, 64 rows per wavefront,
+    # 256-row query tiles): several tile pairs, a ragged last tile, an odd
+    # middle tile, and a non-causal S_q != S_kv case
+    (1, 1000, 1000, 4, 4, 128, True),
+    (2, 700, 700, 6, 2, 128, True),
+    (1, 300, 500, 3, 1, 128, False),
+    # head_dim 128, two-head workgroups, non-causal with more keys than rows
+    (1, 600, 900, 8, 4, 128, False),
 ]
 
 
@@ -105,6 +113,17 @@ def test_large_logits():
     say("large logits")
     for causal in (True, False):
         assert_parity(gpu_prefill(q, k, v, causal), oracle.prefill(q, k, v, causal), "large")
+
+
+def test_large_logits_one_head_workgroups():
+    """The overflow rerun on one-head (64 rows per wavefront) workgroups."""
+    B, S, H_q, H_kv, D = 1, 600, 3, 1, 128
+    q = _rand((B, S, H_q, D), 21, 3.0)
+    k = _rand((B, S, H_kv, D), 22, 3.0)
+    v = _rand((B, S, H_kv, D), 23)
+    say("large logits, one-head workgroups")
+    for causal in (True, False):
+        assert_parity(gpu_prefill(q, k, v, causal), oracle.prefill(q, k, v, causal), "large HP1")
 
 
 def test_increasing_logits():
