@@ -329,7 +329,7 @@ struct Dual {
     dev::short4_t vr[16];
     f32x16_t acc[2];
     float x[32], y[32];
-    float ls[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};  // two running partial row sums per block
+    float ls[2][2];  // two running partial row sums per block
     // K k-step ks feeds chunks 2ks, 2ks+1; V operand op (= c * 4 + dt) feeds
     // chunks 16 + 2op, 17 + 2op and takes two transposed reads
     auto read_k = [&](int ks) { kf[ks] = *reinterpret_cast<const half8_t*>(kb + 16 * ks); };
@@ -360,7 +360,9 @@ struct Dual {
       if (i >= 3 && (i & 1)) {
         const int e = i - 3, g = e >> 4, r = e & 15;
         put_pair<PAR>(g, r, y[e], y[e + 1]);
-        ls[g][(r >> 1) & 1] += y[e] + y[e + 1];
+        // the first pair of each partial sum starts it (no add of zero)
+        if (r < 4) ls[g][(r >> 1) & 1] = y[e] + y[e + 1];
+        else ls[g][(r >> 1) & 1] += y[e] + y[e + 1];
         // keep the add in this chunk (otherwise it sinks to the loop latch)
         asm volatile("" : "+v"(ls[g][(r >> 1) & 1]));
       }
