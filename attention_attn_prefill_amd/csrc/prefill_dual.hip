@@ -28,7 +28,9 @@
 //     S(u+1) = K(u+1) Q^T            16 MFMAs, 8 K operand reads
 //     P(u)   = exp2(S(u)), row sums  ~100 VALU instructions
 //     O     += V(u-1)^T P(u-1)^T    16 MFMAs, 8 V operands (16 reads)
-// which are independent of each other, in one basic block.
+// which are independent of each other, in one basic block, interleaved
+// chunk by chunk (one MFMA and its share of the softmax per chunk; the LDS
+// reads in the even chunks, which carry no fp16 packing or row-sum adds).
 //
 // Scores stay exact: S^T accumulates the fp16 products of Q and K in fp32
 // from zero, and the weight of a key is exp2(s * log2(e)/sqrt(D) - m) with m
@@ -49,18 +51,19 @@
 // rounding to fp16.
 //
 // Staging: K and V tiles of 64 keys, double-buffered in LDS, row-major
-// (K [64][D+8], V [64][D+32]: the padding keeps the operand reads free of
-// bank conflicts), loaded through buffer resources over the kv head's rows
-// [0, S_kv) (rows past the end read as zero and are masked).  K runs one
-// tile ahead of V: the two steps of iteration t read K(t+1) and V(t); during
-// iteration t the tiles K(t+2) and V(t+1), loaded into registers during
-// iteration t-1, are written to the slots that K(t) and V(t-1) held, and
-// one LDS barrier ends the iteration.
+// (K [64][D+8], V [64][D+32]: the padding keeps the operand reads nearly
+// free of bank conflicts), copied from HBM straight into LDS by buffer
+// loads over the kv head's rows [0, S_kv) (rows past the end read as zero
+// and are masked).  K runs one tile ahead of V: the two steps of iteration
+// t read K(t+1) and V(t); the first step copies K(t+2) and the second
+// V(t+1) into the slots that K(t) and V(t-1) held, and a vmcnt(0) wait and
+// one LDS barrier end the iteration.
 //
-// Causal: a wavefront computes sub-blocks up to its diagonal and only the
-// last one (two for 64-row blocks) is masked element-wise; tiles above the
-// workgroup's last row are never loaded.  A workgroup runs query tiles i and
-// n-1-i back to back, so every workgroup does the same work.
+// Causal: all four wavefronts run every step of the workgroup's key range;
+// sub-blocks before a wavefront's diagonal run unmasked, the rest with the
+// element mask (those past the diagonal come out all zero); tiles above the
+// workgroup's last row are never loaded.  A workgroup runs query tiles
+// n-1-i and i back to back, so every workgroup does the same work.
 #include "gfx950_device.h"
 
 #include <math.h>
