@@ -65,6 +65,7 @@
 // workgroup's last row are never loaded.  A workgroup runs query tiles
 // n-1-i and i back to back, so every workgroup does the same work.
 #include "gfx950_device.h"
+#include "q_norm_rope.h"
 
 #include <math.h>
 
@@ -84,7 +85,9 @@ constexpr int kTile = 64;              // keys per staged K/V tile
 constexpr float kShareMax = 32768.0f;  // largest row-sum share that keeps fp16 weights finite
 constexpr uint32_t kPadOffset = 0x80000000u;  // a load offset past any buffer range
 
-template <bool CAUSAL, int HP>
+// ROPE: Q's per-head RMSNorm and NeoX rotation are applied as it is loaded
+// (attn_prefill_qk_norm_rope); the rest of the kernel is unchanged.
+template <bool CAUSAL, int HP, bool ROPE>
 struct Dual {
   static constexpr int D = 128;
   static constexpr int KS = D / 16;                          // k-steps of QK^T
@@ -139,6 +142,12 @@ struct Dual {
   float c2;            // log2(e) / sqrt(D)
   float l[2], lsum[2];
   float share_max;     // largest row-sum share of this lane so far
+  // ROPE: the norm + rotation state of a query row (the two blocks of a
+  // two-head workgroup share their row; a one-head workgroup's blocks take
+  // it in turn) and whether each row's position was valid (else its output
+  // is NaN)
+  qnr::QNormRope<D> qr;
+  bool q_ok[2];
 
   // ---- staging -----------------------------------------------------------
   // Tiles go from HBM straight into LDS (buffer loads with the LDS bit), in
@@ -528,7 +537,6 @@ struct Dual {
   // Q fragments (B operand of S^T = K Q^T: q[row][16*ks + 8*hf + 0..7])
   // and the copies of K(0), V(0), K(1) into LDS; the caller waits for them.
   // Loads per wavefront: 2 * KS for Q, 2 * K_COPIES + V_COPIES copies.
-  static constexpr int TILE_LOADS = 2 * KS + 2 * K_COPIES + V_COPIES;
   __device__ __forceinline__ void issue_tile_loads(const PrefillArgs& a) {
     const int64_t q_row_stride = (int64_t)a.H_q * D;
 #pragma unroll
@@ -542,6 +550,25 @@ struct Dual {
     copy_tiles(0, 0);
 #pragma unroll
     for (int n = 0; n < K_COPIES; ++n) copy(n, 1, 0);
+  }
+  // ROPE: the loads of the row blocks' norm weights, positions and table
+  // rows, and the arithmetic once they (and the Q fragments) are in
+  __device__ __forceinline__ void rope_issue(const PrefillArgs& a) {
+    if constexpr (ROPE) {
+      qr.issue(a, b, row0[0] + col, hf);
+      if (a.positions) qr.tables(a, hf);
+    }
+  }
+  __device__ __forceinline__ void rope_apply(const PrefillArgs& a) {
+    if constexpr (ROPE) {
+      q_ok[0] = qr.apply(a, qf[0]);
+      if (HP == 1) {
+        // the second block's rows (32 further on) in turn
+        qr.issue(a, b, row0[1] + col, hf);
+        if (a.positions) qr.tables(a, hf);
+      }
+      q_ok[1] = qr.apply(a, qf[1]);
+    }
   }
 
   // the whole query tile: first pass, and the recomputation when a
@@ -573,6 +600,7 @@ struct Dual {
           half4_t out;
 #pragma unroll
           for (int j = 0; j < 4; ++j) out[j] = (_Float16)(o[g][dt][rg * 4 + j] * inv);
+          if (ROPE && !q_ok[g]) out = __builtin_bit_cast(half4_t, 0x7e007e007e007e00ull);  // quiet NaN bits
           *reinterpret_cast<half4_t*>(ot + col * OROW + dt * 32 + rg * 8 + hf * 4) = out;
         }
       }
@@ -608,9 +636,9 @@ struct Dual {
 // middle tile runs alone.  Both tiles read the same kv head, so the K/V side
 // is set up once.  The second tile's Q loads and first K/V copies go out
 // before the first tile's epilogue, which then overlaps their latency.
-template <bool CAUSAL, int HP>
+template <bool CAUSAL, int HP, bool ROPE>
 __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a) {
-  using W = Dual<CAUSAL, HP>;
+  using W = Dual<CAUSAL, HP, ROPE>;
   constexpr int D = W::D;
   __shared__ __attribute__((aligned(16))) _Float16 smem[W::SMEM_HALFS];
   __shared__ __attribute__((aligned(16))) _Float16 osmem[W::OUT_LDS];
@@ -655,7 +683,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
 
   w.setup(a, hi, hg);
   w.issue_tile_loads(a);
+  w.rope_issue(a);
   dev::wait_vmcnt0();
+  w.rope_apply(a);
   dev::lds_barrier();
   w.compute(flags);
   if (lo < hi) {
@@ -665,30 +695,47 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
     const int heads[2] = {w.head[0], w.head[1]};
     w.setup(a, lo, hg);
     w.issue_tile_loads(a);
-    if (w.epilogue(a, rows0, heads)) dev::wait_vmcnt<2 * (D / 8) * 32 / 64>();  // its 16 stores may stay in flight
-    else dev::wait_vmcnt0();
+    const bool full = w.epilogue(a, rows0, heads);
+    if (ROPE) {
+      // the rotation's loads go out once the first tile's outputs (and their
+      // registers) are gone; loads retire in order, so waiting for them
+      // waits for the 16 output stores as well
+      w.rope_issue(a);
+      dev::wait_vmcnt0();
+      w.rope_apply(a);
+    } else if (full) {
+      dev::wait_vmcnt<2 * (D / 8) * 32 / 64>();  // its 16 stores may stay in flight
+    } else {
+      dev::wait_vmcnt0();
+    }
     dev::plain_barrier();  // every wavefront's copies of the second tile have landed
     w.compute(flags);
   }
   w.epilogue(a, w.row0, w.head);
 }
 
-template <bool CAUSAL, int HP>
+template <bool CAUSAL, int HP, bool ROPE>
 hipError_t launch_dual_t(const PrefillArgs& a_in, hipStream_t stream) {
   PrefillArgs a = a_in;
-  a.n_qtiles = (a.S_q + Dual<CAUSAL, HP>::ROWS_WG - 1) / Dual<CAUSAL, HP>::ROWS_WG;
+  constexpr int ROWS_WG = Dual<CAUSAL, HP, ROPE>::ROWS_WG;
+  a.n_qtiles = (a.S_q + ROWS_WG - 1) / ROWS_WG;
   const int64_t blocks = (int64_t)((a.n_qtiles + 1) / 2) * (a.H_q / HP) * a.B;
   void* kargs[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_dual_kernel<CAUSAL, HP>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_dual_kernel<CAUSAL, HP, ROPE>),
                          dim3((unsigned)blocks), dim3(kThreads), kargs, 0, stream);
+}
+
+template <bool ROPE>
+hipError_t launch_dual_r(const PrefillArgs& a, bool causal, hipStream_t stream) {
+  const bool pair = ((a.H_q / a.H_kv) % 2) == 0;
+  if (causal) return pair ? launch_dual_t<true, 2, ROPE>(a, stream) : launch_dual_t<true, 1, ROPE>(a, stream);
+  return pair ? launch_dual_t<false, 2, ROPE>(a, stream) : launch_dual_t<false, 1, ROPE>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_dual(const PrefillArgs& a, bool causal, hipStream_t stream) {
-  const bool pair = ((a.H_q / a.H_kv) % 2) == 0;
-  if (causal) return pair ? launch_dual_t<true, 2>(a, stream) : launch_dual_t<true, 1>(a, stream);
-  return pair ? launch_dual_t<false, 2>(a, stream) : launch_dual_t<false, 1>(a, stream);
+  return a.cos_table ? launch_dual_r<true>(a, causal, stream) : launch_dual_r<false>(a, causal, stream);
 }
 
 }  // namespace attn

@@ -52,6 +52,7 @@
 //     once per wavefront, so this costs nothing next to the tile loop;
 //     K is rotated once, by the pass that also writes it to the cache.
 #include "attn_internal.h"
+#include "q_norm_rope.h"
 
 #include <math.h>
 
@@ -222,90 +223,6 @@ __device__ __forceinline__ void qk_tile(f32x16_t (&s)[2], const _Float16* kl, co
     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
   }
 }
-
-// RMSNorm (when q_weight is set) and NeoX rotation of the Q fragment of one
-// lane (dims 16 ks + 8 hf + j of its query row), in fp32, rounded to fp16
-// once.  Its loads go out in two waves so that their latency overlaps the
-// first K/V tile loads: the weight slices and the position with the Q loads
-// (issue), the table rows once the position is known (tables), then the
-// arithmetic (apply).  Without a positions array the position is the row's
-// index in its sequence and the table rows go out with the Q loads too.  Rows past S_q stay zero.  apply() returns false for a
-// position outside [0, max_pos): that row's fragment is zero (this file is
-// built without NaN semantics, so no NaN enters the arithmetic) and the
-// epilogue stores NaN bits for it.  Every lane of the wavefront takes part
-// in apply() (the row sum is exchanged with lane l ^ 32).
-template <int D>
-struct QNormRope {
-  static constexpr int KS = D / 16, HK = KS / 2;
-  half8_t w[KS];
-  f32x4_t c[HK][2], s[HK][2];
-  int pos;
-  bool valid, ok;
-
-  __device__ __forceinline__ void issue(const PrefillArgs& a, int b, int qrow, int hf) {
-    valid = qrow < a.S_q;
-    if (a.positions) {
-      pos = valid ? a.positions[(int64_t)b * a.S_q + qrow] : 0;
-    } else {
-      pos = qrow;
-      tables(a, hf);
-    }
-    if (a.q_weight) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const half8_t*>(a.q_weight + 16 * ks + 8 * hf);
-    }
-  }
-  __device__ __forceinline__ void tables(const PrefillArgs& a, int hf) {
-    ok = pos >= 0 && pos < a.max_pos;
-    const int64_t trow = (int64_t)(ok ? pos : 0) * (D / 2);
-#pragma unroll
-    for (int ks = 0; ks < HK; ++ks) {
-      const f32x4_t* ct = reinterpret_cast<const f32x4_t*>(a.cos_table + trow + 16 * ks + 8 * hf);
-      const f32x4_t* st = reinterpret_cast<const f32x4_t*>(a.sin_table + trow + 16 * ks + 8 * hf);
-      c[ks][0] = ct[0];
-      c[ks][1] = ct[1];
-      s[ks][0] = st[0];
-      s[ks][1] = st[1];
-    }
-  }
-  __device__ __forceinline__ bool apply(const PrefillArgs& a, half8_t (&qf)[KS]) const {
-    float y[KS][8];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) y[ks][j] = (float)qf[ks][j];
-    if (a.q_weight) {
-      float ss = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(y[ks][j], y[ks][j], ss);
-      ss = wave_half_swap_add(ss);
-      // v_rsq_f32 directly: the math library's rsqrtf is not inlined into
-      // this file (built without NaN semantics) and would become a call; for
-      // the normal arguments a mean square plus eps gives, it is the same
-      // instruction
-      const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) y[ks][j] = y[ks][j] * inv * (float)w[ks][j];
-    }
-#pragma unroll
-    for (int ks = 0; ks < HK; ++ks) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float cj = c[ks][j >> 2][j & 3], sj = s[ks][j >> 2][j & 3];
-        const float lo = y[ks][j], hi = y[ks + HK][j];
-        const float rlo = fmaf(lo, cj, -hi * sj);
-        const float rhi = fmaf(hi, cj, lo * sj);
-        qf[ks][j] = (valid && ok) ? (_Float16)rlo : (_Float16)0.0f;
-        qf[ks + HK][j] = (valid && ok) ? (_Float16)rhi : (_Float16)0.0f;
-      }
-    }
-    return !valid || ok;
-  }
-};
 
 // Issue order of a GEMM phase: kLdsAhead operand reads first, then each
 // MFMA followed by up to two more reads, so the LDS reads of later operands
@@ -524,7 +441,7 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
     for (int ks = 0; ks < P::KS; ++ks) p.qf[ks] = half8_t{};
   }
   // the row's position and the norm weights go out with the Q loads
-  QNormRope<D> qr;
+  qnr::QNormRope<D> qr;
   if constexpr (ROPE) qr.issue(a, b, p.qrow, p.hf);
 #pragma unroll
   for (int dt = 0; dt < P::DT; ++dt) p.o[dt] = f32x16_t{};
@@ -713,7 +630,7 @@ hipError_t launch_hp(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a_in, int head_dim, bool causal, hipStream_t stream) {
-  if (head_dim == 128 && !a_in.cos_table) return launch_prefill_dual(a_in, causal, stream);
+  if (head_dim == 128) return launch_prefill_dual(a_in, causal, stream);
   PrefillArgs a = a_in;
   a.n_qtiles = (a.S_q + kBlockM - 1) / kBlockM;
   switch (head_dim) {

@@ -63,9 +63,10 @@ def parse():
 KERNEL_SOURCES = {
     "prefill_dual_kernel": ["attention_attn_prefill_amd/csrc/prefill_dual.hip",
                             "attention_attn_prefill_amd/csrc/gfx950_device.h",
+                            "attention_attn_prefill_amd/csrc/q_norm_rope.h",
                             "attention_attn_prefill_amd/csrc/attn_internal.h"],
     "prefill_fwd_kernel": ["attention_attn_prefill_amd/csrc/prefill_fwd.hip",
-                           "attention_attn_prefill_amd/csrc/gfx950_device.h",
+                           "attention_attn_prefill_amd/csrc/q_norm_rope.h",
                            "attention_attn_prefill_amd/csrc/attn_internal.h"],
     "decode_split_kernel": ["attention_attn_prefill_amd/csrc/decode_paged.hip",
                             "attention_attn_prefill_amd/csrc/attn_internal.h"],

@@ -219,6 +219,12 @@ PREFILL_ROPE_CASES = [  # B, S_q, S_kv, H_q, H_kv, D, causal, norm, theta
     (1, 200, 200, 3, 1, 128, True, False, 1e4),    # one head per workgroup, rotation only
     (2, 77, 150, 4, 2, 64, False, True, 1e4),      # non-causal, S_q != S_kv
     (3, 64, 96, 8, 8, 32, False, True, 5e5),       # D = 32
+    # head_dim 128: one head per workgroup with the norm over several
+    # query-tile pairs (the second tile's rotation after the first's
+    # epilogue), non-causal S_q != S_kv, and four tile pairs on two heads
+    (1, 600, 600, 3, 1, 128, True, True, 1e6),
+    (2, 180, 420, 8, 4, 128, False, True, 1e4),
+    (1, 1000, 1000, 16, 8, 128, True, True, 1e6),
 ]
 
 
@@ -271,10 +277,11 @@ def test_prefill_with_q_norm_rope_on_load(B, S_q, S_kv, H_q, H_kv, D, causal, no
     assert_parity(got, host(to).astype(np.float64), "on-load vs two-pass")
 
 
-def test_prefill_q_rope_bad_positions_give_nan_rows():
+@pytest.mark.parametrize("H_q,H_kv", [(4, 2), (3, 1)])
+def test_prefill_q_rope_bad_positions_give_nan_rows(H_q, H_kv):
     """Query rows whose position has no table row come out NaN; the other
-    rows are unaffected."""
-    B, S, H_q, H_kv, D, max_pos = 1, 130, 4, 2, 128, 512
+    rows are unaffected (two-head and one-head workgroups)."""
+    B, S, D, max_pos = 1, 130, 128, 512
     q, k, v = _rand((B, S, H_q, D), 61), _rand((B, S, H_kv, D), 62), _rand((B, S, H_kv, D), 63)
     pos = np.arange(S, dtype=np.int32)
     pos[[3, 64, 129]] = [-1, max_pos, 1 << 30]
