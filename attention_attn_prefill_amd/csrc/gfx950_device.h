@@ -32,18 +32,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int b
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-__device__ __forceinline__ half8_t buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
-  return __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
-}
-
 // Buffer load of 16 bytes per lane straight into LDS: lane i's bytes land at
-// lds + 16 * i (one contiguous 1 KB block per wavefront; lds must be the
-// same for every lane).  Completion is counted by vmcnt.
-__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, _Float16* lds, int offset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, offset, 0, 0, 0);
-}
-
-// The same with the LDS destination given as a byte address in LDS (uniform).
+// LDS byte address lds_addr + 16 * i (one contiguous 1 KB block per
+// wavefront; lds_addr is uniform).  Completion is counted by vmcnt.
 __device__ __forceinline__ void buffer_load16_lds_at(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, int offset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds_addr, 16, offset, 0,
                                            0, 0);
@@ -90,21 +81,12 @@ __device__ __forceinline__ short4_t lds_read_tr(const _Float16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
 }
 
-// PV operand V^T[32 dims x 16 keys] for lane l: dims dt*32 + l%32, keys
-// 16c + 4*hf + (0..3) then 16c + 8 + 4*hf + (0..3) -- the key order of the
-// B operand taken straight from an S^T accumulator (registers 8(c%2)..+7 of
-// the 32-key block c/2).  `vl` already holds this lane's row/column offset.
-template <int VROW>
-__device__ __forceinline__ half8_t pv_operand(const _Float16* vl, int dt, int c) {
-  const short4_t lo = lds_read_tr(vl + 16 * c * VROW + dt * 32);
-  const short4_t hi = lds_read_tr(vl + (16 * c + 8) * VROW + dt * 32);
-  const short4_t lohi[2] = {lo, hi};
-  return __builtin_bit_cast(half8_t, lohi);
-}
-
 // Lane offset (halfs) of the transposed V read in a V tile of row stride
 // VROW: 16-lane group G = lane/16 covers dims 16*(G%2)..+15 of keys
-// 4*hf + (lane%16)/4, four dims per lane.
+// 4*hf + (lane%16)/4, four dims per lane.  Two such reads, 8 keys apart,
+// form the PV operand V^T[32 dims x 16 keys]: dims dt*32 + l%32, keys
+// 16c + 4*hf + (0..3) then 16c + 8 + 4*hf + (0..3) -- the key order of the
+// B operand taken straight from an S^T accumulator.
 template <int VROW>
 __device__ __forceinline__ int pv_lane_offset(int lane) {
   const int hf = lane >> 5;

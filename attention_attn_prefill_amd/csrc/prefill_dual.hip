@@ -285,28 +285,6 @@ struct Dual {
     share_max = fmaxf(share_max, fmaxf(lsum[0], lsum[1]));
   }
 
-  // softmax of sub-block uu (parity PAR) against the fixed reference
-  template <int PAR, bool MASK>
-  __device__ __forceinline__ void softmax(int uu) {
-    if (MASK) mask<PAR>(uu);
-    weights<PAR>();
-  }
-
-  // O^T += V^T P^T for sub-block uu (parity PAR) from V tile uu/2
-  template <int PAR>
-  __device__ __forceinline__ void pv(int uu) {
-    const _Float16* vl = smem + 2 * K_LDS + ((uu >> 1) & 1) * V_LDS + v_lane;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const half8_t vf = dev::pv_operand<VROW>(vl, dt, 2 * PAR + c);
-#pragma unroll
-        for (int g = 0; g < 2; ++g) o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p_chunk<PAR>(g, c), o[g][dt], 0, 0, 0);
-      }
-    }
-  }
-
   // Step u (parity PAR) of the loop: S(u+1) = K Q^T into s[PAR ^ 1], the
   // softmax of s[PAR] into p[PAR], and O += V^T P(u-1)^T.  STAGE 1 issues
   // the iteration's K tile copies in the first chunks of the step, STAGE 2
