@@ -294,10 +294,12 @@ struct Dual {
   // The three parts are independent, and a wavefront is alone on its SIMD,
   // so the instruction order is spelled out: 32 chunks, each one MFMA (16 of
   // QK, then 16 of PV), the fma of one score element, the exponential of the
-  // element before it, every other chunk the fp16 pair and the row-sum add
-  // of two earlier elements, and the LDS operand reads about six MFMAs
-  // before their use.  A scheduling fence after every chunk keeps the
-  // compiler from regrouping MFMAs and VALU work into runs.
+  // element before it, every other (odd) chunk the fp16 pair and the
+  // row-sum adds of two earlier elements, and in the even chunks the LDS
+  // operand reads, six to eight MFMAs before their use.  A scheduling fence
+  // after every chunk keeps the compiler from regrouping MFMAs and VALU work
+  // into runs.
+  //
   // The first K operands of a step are read AHEAD / 2 = 3 k-steps ahead of
   // its first MFMA.  The second step of an iteration reads the same K tile
   // as the first, already resident, so the first step reads them for it in
