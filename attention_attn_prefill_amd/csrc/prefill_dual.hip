@@ -594,16 +594,20 @@ struct Dual {
     constexpr int ROWS_PER = 64 / PIECES;  // rows per 64-lane store
     const int pr = lane / PIECES, pc = lane % PIECES;
     const bool full = rows0[1] + 31 < a.S_q;
+    // all of a block's row pieces are read back before its stores go out, so
+    // the LDS reads overlap instead of each waiting before its own store
+    constexpr int PER_G = 32 / ROWS_PER;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const _Float16* ot = osmem + (wave * 2 + g) * 32 * OROW;
+      half8_t v8[PER_G];
 #pragma unroll
-      for (int i = 0; i < 32 / ROWS_PER; ++i) {
-        const int r = i * ROWS_PER + pr;
-        const int row = rows0[g] + r;
-        const half8_t v8 = *reinterpret_cast<const half8_t*>(ot + r * OROW + 8 * pc);
+      for (int i = 0; i < PER_G; ++i) v8[i] = *reinterpret_cast<const half8_t*>(ot + (i * ROWS_PER + pr) * OROW + 8 * pc);
+#pragma unroll
+      for (int i = 0; i < PER_G; ++i) {
+        const int row = rows0[g] + i * ROWS_PER + pr;
         if (full || row < a.S_q)
-          *reinterpret_cast<half8_t*>(a.o + ((int64_t)b * a.S_q + row) * q_row_stride + (int64_t)heads[g] * D + 8 * pc) = v8;
+          *reinterpret_cast<half8_t*>(a.o + ((int64_t)b * a.S_q + row) * q_row_stride + (int64_t)heads[g] * D + 8 * pc) = v8[i];
       }
     }
     return full;
