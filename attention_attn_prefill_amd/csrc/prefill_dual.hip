@@ -131,6 +131,11 @@ struct Dual {
   int S_kv;
   int mask_from;  // first sub-block that may need the element mask
   int n_tiles;    // K/V tiles the workgroup stages
+  // K/V tile t of the pass sits in slot (t + par0) & 1.  Copies of tiles
+  // next_base and next_base + 1 (past the pass's keys) fetch the next query
+  // tile's tiles 0 and 1 instead (next_base is out of reach otherwise).
+  int par0;
+  int next_base;
   int row0[2];    // first query row of each row block
   int head[2];    // query head of each row block
   int b;          // batch entry
@@ -184,12 +189,14 @@ struct Dual {
   // copy n of the tile pair (K tile tk, V tile tv); n < COPIES
   __device__ __forceinline__ void copy(int n, int tk, int tv) {
     if (n < K_COPIES) {
-      const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)tk * kTile * row_bytes);
-      dev::buffer_load16_lds_at(krsrc, (tk & 1) ? k_dst[1][n] : k_dst[0][n], (int)(k_off[n] + base));
+      const int src_t = tk >= next_base ? tk - next_base : tk;
+      const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)src_t * kTile * row_bytes);
+      dev::buffer_load16_lds_at(krsrc, ((tk + par0) & 1) ? k_dst[1][n] : k_dst[0][n], (int)(k_off[n] + base));
     } else {
       const int j = n - K_COPIES;
-      const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)tv * kTile * row_bytes);
-      dev::buffer_load16_lds_at(vrsrc, (tv & 1) ? v_dst[1][j] : v_dst[0][j], (int)(v_off[j] + base));
+      const int src_t = tv >= next_base ? tv - next_base : tv;
+      const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)src_t * kTile * row_bytes);
+      dev::buffer_load16_lds_at(vrsrc, ((tv + par0) & 1) ? v_dst[1][j] : v_dst[0][j], (int)(v_off[j] + base));
     }
   }
   __device__ __forceinline__ void copy_tiles(int tk, int tv) {
@@ -213,7 +220,7 @@ struct Dual {
   // row blocks, into s[PAR] (raw dot products, fp32)
   template <int PAR>
   __device__ __forceinline__ void qk(int uu) {
-    const _Float16* kb = smem + ((uu >> 1) & 1) * K_LDS + k_lane + PAR * 32 * KROW;
+    const _Float16* kb = smem + (((uu >> 1) + par0) & 1) * K_LDS + k_lane + PAR * 32 * KROW;
     half8_t kf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const half8_t*>(kb + 16 * ks);
@@ -315,8 +322,8 @@ struct Dual {
 #pragma unroll
     for (int g = 0; g < 2; ++g) l[g] += lsum[g];
     if (MASK) mask<PAR>(u);
-    const _Float16* kb = smem + (((u + 1) >> 1) & 1) * K_LDS + k_lane + PP * 32 * KROW;
-    const _Float16* vl = smem + 2 * K_LDS + (((u - 1) >> 1) & 1) * V_LDS + v_lane;
+    const _Float16* kb = smem + ((((u + 1) >> 1) + par0) & 1) * K_LDS + k_lane + PP * 32 * KROW;
+    const _Float16* vl = smem + 2 * K_LDS + ((((u - 1) >> 1) + par0) & 1) * V_LDS + v_lane;
     half8_t kf[KS];
     dev::short4_t vr[16];
     f32x16_t acc[2];
@@ -335,7 +342,7 @@ struct Dual {
       else read_k(ks);
     }
     // the next step's K sub-block (u + 2, parity PAR), for PRE_OUT
-    const _Float16* kb_next = smem + (((u + 2) >> 1) & 1) * K_LDS + k_lane + PAR * 32 * KROW;
+    const _Float16* kb_next = smem + ((((u + 2) >> 1) + par0) & 1) * K_LDS + k_lane + PAR * 32 * KROW;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -514,9 +521,11 @@ struct Dual {
     n_tiles = (n_sub_wg + 1) / 2;
   }
 
-  // Q fragments (B operand of S^T = K Q^T: q[row][16*ks + 8*hf + 0..7])
-  // and the copies of K(0), V(0), K(1) into LDS; the caller waits for them.
-  // Loads per wavefront: 2 * KS for Q, 2 * K_COPIES + V_COPIES copies.
+  // Q fragments (B operand of S^T = K Q^T: q[row][16*ks + 8*hf + 0..7]),
+  // and with COPIES the copies of K(0), V(0), K(1) into LDS; the caller
+  // waits for them.  Loads per wavefront: 2 * KS for Q, 2 * K_COPIES +
+  // V_COPIES copies.
+  template <bool COPIES>
   __device__ __forceinline__ void issue_tile_loads(const PrefillArgs& a) {
     const int64_t q_row_stride = (int64_t)a.H_q * D;
 #pragma unroll
@@ -527,9 +536,11 @@ struct Dual {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[g][ks] = *reinterpret_cast<const half8_t*>(qp + 16 * ks);
     }
-    copy_tiles(0, 0);
+    if (COPIES) {
+      copy_tiles(0, 0);
 #pragma unroll
-    for (int n = 0; n < K_COPIES; ++n) copy(n, 1, 0);
+      for (int n = 0; n < K_COPIES; ++n) copy(n, 1, 0);
+    }
   }
   // ROPE: the loads of the row blocks' norm weights, positions and table
   // rows, and the arithmetic once they (and the Q fragments) are in
@@ -666,19 +677,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
   w.copy_dsts();
 
   w.setup(a, hi, hg);
-  w.issue_tile_loads(a);
+  w.par0 = 0;
+  // both tiles read the same K/V rows from key 0 on: the first pass's last
+  // two iterations copy the second tile's K(0), V(0), K(1) (see next_base)
+  w.next_base = lo < hi ? w.n_tiles : 0x40000000;
+  w.template issue_tile_loads<true>(a);
   w.rope_issue(a);
   dev::wait_vmcnt0();
   w.rope_apply(a);
   dev::lds_barrier();
   w.compute(flags);
   if (lo < hi) {
-    // the K/V slots are free (the last pass ended with a barrier) and the Q
-    // fragments dead: start the second tile's loads, then store the first
+    // K(0), V(0), K(1) of the second tile are in LDS already (the first
+    // pass's last iterations copied them, in the slots after its own last
+    // tiles) and the Q fragments are dead: start the second tile's Q loads,
+    // then store the first tile
     const int rows0[2] = {w.row0[0], w.row0[1]};
     const int heads[2] = {w.head[0], w.head[1]};
+    const int n_first = w.n_tiles;
     w.setup(a, lo, hg);
-    w.issue_tile_loads(a);
+    w.par0 = n_first & 1;
+    w.next_base = 0x40000000;
+    w.template issue_tile_loads<false>(a);
     const bool full = w.epilogue(a, rows0, heads);
     if (ROPE) {
       // the rotation's loads go out once the first tile's outputs (and their
@@ -692,7 +712,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
     } else {
       dev::wait_vmcnt0();
     }
-    dev::plain_barrier();  // every wavefront's copies of the second tile have landed
+    dev::plain_barrier();
     w.compute(flags);
   }
   w.epilogue(a, w.row0, w.head);
