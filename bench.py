@@ -57,6 +57,11 @@ def parse():
                         "and with --workload grpo only the shared-prefix calls")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle sample")
+    p.add_argument("--prefill-sweep", action="store_true",
+                   help="instead of the step: causal head_dim-128 prefill at 256 workgroups "
+                        "(S = 1024/2048/4096/8192, B = 8/4/2/1, H_q 16, H_kv 8), whose "
+                        "workgroups run 18/34/66/130 64-key iterations, and the fit "
+                        "time = fixed + iterations x per-iteration cost")
     return p.parse_args()
 
 
@@ -463,6 +468,45 @@ def main_grpo(args):
     print(json.dumps(leg), flush=True)
 
 
+def main_sweep(args):
+    """Fixed and per-iteration cost of the head_dim-128 causal prefill.  At
+    S = 128 n (n even) with B = 2048 / S, H_q 16 and H_kv 8 the grid is
+    n/2 query-tile pairs x 8 head pairs x B = 256 workgroups, one per CU, and
+    every workgroup runs 2n + 2 iterations of 64 keys (tile j of a pair has
+    keys up to 128 (j + 1)).  Times are the pages' method (HIP events around
+    back-to-back launches), so the fixed part includes the gap between
+    launches."""
+    import torch
+
+    from attention_attn_prefill_amd import attn_prefill
+    from attention_attn_prefill_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for S, B in ((1024, 8), (2048, 4), (4096, 2), (8192, 1)):
+        cfg = W.PrefillConfig(f"sweep_{S}", 90 + S // 1024, B, S, S, 16, 8, 128, True)
+        q, k, v = (torch.from_numpy(x).to(dev) for x in W.prefill_inputs(cfg))
+        o = torch.empty_like(q)
+        iters = 2 * (S // 128) + 2
+        fn = lambda: attn_prefill(q, k, v, o, causal=True)  # noqa: E731
+        t0 = time.time()
+        while time.time() - t0 < 1.0:
+            fn()
+        torch.cuda.synchronize()
+        ms, reps = pages_method(fn, stream, iters=50, warm=args.warmup, repeats=7)
+        rows.append({"S": S, "B": B, "workgroups": (S // 256) * 8 * B, "iterations_per_workgroup": iters,
+                     "us": round(ms * 1e3, 2), "tflops": round(cfg.flops / ms / 1e9, 1)})
+        print(f"[sweep] S={S} B={B}: {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
+    x = np.array([r["iterations_per_workgroup"] for r in rows], np.float64)
+    y = np.array([r["us"] for r in rows], np.float64)
+    c, f = np.polyfit(x, y, 1)
+    print(json.dumps({"mode": "prefill_sweep", "kernel": "prefill_dual_kernel<128,causal>",
+                      "method": "HIP events around 50 back-to-back launches, median of 7",
+                      "rows": rows, "fit": {"fixed_us_per_workgroup": round(float(f), 2),
+                                            "us_per_iteration": round(float(c), 4)}}))
+
+
 def calibration_copy(dev):
     import torch
     src = torch.ones(256 << 20, dtype=torch.float16, device=dev)
@@ -480,6 +524,9 @@ def main():
               "this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
+    if args.prefill_sweep:
+        main_sweep(args)
+        return
     if args.workload == "grpo":
         main_grpo(args)
         return
