@@ -39,15 +39,30 @@ attn_status_t check_decode_shape(int num_seqs, int H_q, int H_kv, int head_dim,
 struct DecodePlan {
   int split_blocks;
   int n_split_max;
+  bool balanced;    // equal runs of the (sequence, kv head, block) order
   size_t ws_bytes;  // 0 when no merge pass is needed
 };
 
+// Plain decode: one split per (sequence, kv head) when the table is short
+// enough for that to fill the chip (no workspace needed).  Otherwise the
+// balanced mode (up to kDecodeBalancedMaxSeqs sequences, whose block prefix
+// fits LDS): kDecodeWorkers runs, partials in (num_seqs * H_kv +
+// kDecodeWorkers) slots of G heads, then the block prefix.  Beyond that,
+// fixed-length splits with num_seqs * H_q * n_split_max partial slots.
 DecodePlan plan_decode(int num_seqs, int H_q, int H_kv, int max_blocks_per_seq) {
   DecodePlan p;
   p.split_blocks = attn::decode_split_blocks(num_seqs, H_kv, max_blocks_per_seq);
   p.n_split_max = (int)ceil_div64(max_blocks_per_seq, p.split_blocks);
+  p.balanced = false;
   if (p.n_split_max <= 1) {
     p.ws_bytes = 0;
+  } else if (num_seqs <= attn::kDecodeBalancedMaxSeqs &&
+             (int64_t)num_seqs * (max_blocks_per_seq + 16) * H_kv < (int64_t)0x7fffffff &&
+             ((int64_t)num_seqs * H_kv + attn::kDecodeWorkers) * (H_q / H_kv) * (attn::kDecodeHeadDim + 2) <
+                 (int64_t)0x7fffffff) {
+    p.balanced = true;
+    const int64_t slots = ((int64_t)num_seqs * H_kv + attn::kDecodeWorkers) * (H_q / H_kv);
+    p.ws_bytes = (size_t)(slots * (attn::kDecodeHeadDim + 2) + num_seqs + 1) * sizeof(float);
   } else {
     const int64_t slots = (int64_t)num_seqs * H_q * p.n_split_max;
     p.ws_bytes = (size_t)slots * (attn::kDecodeHeadDim + 2) * sizeof(float);
@@ -157,6 +172,7 @@ static attn_status_t decode_paged(const void* q, const void* k_cache, const void
     // single pass: one split covers the whole table width
     plan.split_blocks = max_blocks_per_seq;
     plan.n_split_max = 1;
+    plan.balanced = false;
   } else if (ws_bytes < plan.ws_bytes) {
     return ATTN_ERR_WORKSPACE;
   }
@@ -169,9 +185,13 @@ static attn_status_t decode_paged(const void* q, const void* k_cache, const void
   a.out = static_cast<_Float16*>(out);
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
-  const int64_t slots = (int64_t)num_seqs * H_q * plan.n_split_max;
+  const int64_t slots = plan.balanced
+                            ? ((int64_t)num_seqs * H_kv + attn::kDecodeWorkers) * (H_q / H_kv)
+                            : (int64_t)num_seqs * H_q * plan.n_split_max;
   a.ws_o = plan.n_split_max > 1 ? ws : nullptr;
   a.ws_ml = plan.n_split_max > 1 ? ws + slots * attn::kDecodeHeadDim : nullptr;
+  a.workers = plan.balanced ? attn::kDecodeWorkers : 0;
+  a.run_prefix = plan.balanced ? reinterpret_cast<int32_t*>(ws + slots * (attn::kDecodeHeadDim + 2)) : nullptr;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.H_q = H_q;
@@ -363,6 +383,8 @@ ATTN_EXPORT attn_status_t attn_decode_paged_shared_prefix(
   a.ws_o = static_cast<float*>(workspace);
   a.ws_ml = a.ws_o + slots * attn::kDecodeHeadDim;
   a.seq_skip = reinterpret_cast<int32_t*>(a.ws_ml + slots * 2);
+  a.workers = 0;  // fixed-length splits after the prefix
+  a.run_prefix = nullptr;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.H_q = H_q;

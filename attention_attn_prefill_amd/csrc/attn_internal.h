@@ -63,6 +63,14 @@ struct DecodeArgs {
   // [num_seqs] (workspace): each sequence's prefix blocks, or -1 when its
   // group breaks a checked rule; written by the prefix launch
   int32_t* seq_skip;
+  // Balanced mode (plain decode with partials), off when workers == 0: the
+  // (sequence, kv head, block) order is cut into `workers` equal runs, one
+  // per workgroup; a (sequence, kv head) that one run covers is finished by
+  // it, the others leave partials in slot (s * H_kv + g + run) of ws_o /
+  // ws_ml (G heads per slot) for the merge.  run_prefix [num_seqs + 1]
+  // (workspace) receives the blocks per kv head before each sequence.
+  int workers;
+  int32_t* run_prefix;
 };
 
 struct KvAppendArgs {
@@ -128,6 +136,9 @@ constexpr int kDecodeHeadDim = 128;
 int decode_split_blocks(int num_seqs, int H_kv, int max_blocks_per_seq);
 constexpr int kPrefixChunkBlocks = 64;  // prefix blocks per prefix-kernel workgroup
 constexpr int kDecodeSingleSplitPairs = 2048;  // shared-prefix decode: one split per sequence from here
+constexpr int kDecodeWorkers = 1024;      // balanced decode: runs (4 resident workgroups x 256 CUs)
+constexpr int kDecodeMinRun = 16;         // balanced decode: fewest blocks per run
+constexpr int kDecodeBalancedMaxSeqs = 4096;  // balanced decode: sequences whose prefix fits LDS
 
 // Shared-prefix mode: the group gi of sequence s (group_start ascending,
 // group_start[0] = 0, group_start[num_groups] = num_seqs) and its shared

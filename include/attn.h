@@ -104,7 +104,11 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
  * Bytes of device workspace attn_decode_paged needs for split-K decoding of
  * up to num_seqs sequences with tables max_blocks_per_seq wide.  Returns 0 if
  * no workspace is needed (every sequence fits one split), and 0 for invalid
- * or unsupported arguments (attn_decode_paged reports those).
+ * or unsupported arguments (attn_decode_paged reports those).  The size
+ * depends on the shape only: up to 4096 sequences it is
+ * ((num_seqs * H_kv + 1024) * (H_q / H_kv) * 130 + num_seqs + 1) * 4 bytes,
+ * independent of the table width; beyond that (or past 32-bit positions)
+ * num_seqs * H_q * splits * 130 * 4.
  */
 size_t attn_decode_paged_workspace_size(int num_seqs, int H_q, int H_kv,
                                         int head_dim, int max_blocks_per_seq,
@@ -133,8 +137,14 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int H_q, int H_kv,
  * never reads a block outside [0, num_blocks).
  *
  * workspace: device memory of at least attn_decode_paged_workspace_size(...)
- * bytes selects split-K decoding (sequences cut into fixed token chunks
- * processed in parallel, then merged by log-sum-exp).  NULL selects the
+ * bytes selects split-K decoding (this library's design; the pages' project
+ * memory names flash-decoding split-K as the fix for long contexts): the
+ * visible blocks of every (sequence, kv head) are cut into pieces processed
+ * in parallel, then merged by log-sum-exp.  Up to 4096 sequences the cut is
+ * balanced: every kv head's blocks, sequence after sequence, form equal runs
+ * (one workgroup each, as many as the GPU holds at once), each sequence
+ * charged a fixed cost of 6 blocks so runs over many short sequences take
+ * fewer blocks; beyond that, fixed-length chunks.  NULL selects the
  * single-pass kernel (one workgroup walks a whole sequence).  Both give the
  * same result within fp32 rounding.
  *
@@ -171,8 +181,9 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache,
  * each device it runs on until the process ends.
  *
  *   - A call whose workspace size exceeds ATTN_DECODE_SCRATCH_BYTES returns
- *     ATTN_ERR_WORKSPACE and enqueues nothing (e.g. H_q = 16 allows 64
- *     sequences of 32768 tokens; use attn_decode_paged for more).
+ *     ATTN_ERR_WORKSPACE and enqueues nothing (e.g. H_q = 16, H_kv = 8
+ *     allows up to 1887 sequences of any table width; use attn_decode_paged
+ *     for more).
  *   - The array of the CURRENT device is used; a non-NULL stream must belong
  *     to that device (else ATTN_ERR_INVALID_ARG).  Its device address is
  *     looked up on the first call on each device (under a lock), so make one

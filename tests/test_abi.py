@@ -111,26 +111,35 @@ def decode_scratch(lib, q=P, kc=P, vc=P, out=P2, bt=P, sl=P, num_seqs=4, H_q=16,
     (dict(q=NULL), INV), (dict(out=NULL), INV), (dict(sl=NULL), INV), (dict(num_seqs=0), INV),
     (dict(H_q=12, H_kv=8), INV), (dict(num_blocks=0), INV), (dict(D=64), UNS), (dict(bs=32), UNS),
     (dict(bt=ctypes.c_void_p(0x10002)), INV),
-    # 64 sequences, 4096-block tables, H_q = 16: 16.25 MiB of partials, more
-    # than the library's 16 MiB array
-    (dict(num_seqs=64, max_bps=4096), WS), (dict(num_seqs=128, max_bps=2048), WS),
+    # partials beyond the library's 16 MiB array: 4096 sequences with
+    # 256-block tables at H_q = 16 need 35 MB (a slot per (sequence, kv head)
+    # and per run); 5000 sequences (fixed-length splits) need 83 MB
+    (dict(num_seqs=4096, max_bps=256), WS), (dict(num_seqs=5000, max_bps=256), WS),
 ])
 def test_decode_scratch_rejects(lib, kw, want):
     assert decode_scratch(lib, **kw) == want
 
 
 def test_workspace_size(lib):
-    # 256 sequences x 8 kv heads, tables of 256 blocks: splits of 128 blocks
-    # (2 per sequence); each split slot holds 128 fp32 outputs + (max, sum)
-    assert binding.attn_decode_paged_workspace_size(256, 16, 8, 128, 256, 16) == \
-        256 * 16 * 2 * (128 + 2) * 4
-    # 64 x 8 pairs, 2048-block tables: 16 splits of 128 blocks
-    assert binding.attn_decode_paged_workspace_size(64, 16, 8, 128, 2048, 16) == \
-        64 * 16 * 16 * (128 + 2) * 4
-    # 4 x 8 pairs, 2048-block tables: the largest split that keeps
-    # pairs * splits >= 2048 is 32 blocks (64 splits)
-    assert binding.attn_decode_paged_workspace_size(4, 16, 8, 128, 2048, 16) == \
-        4 * 16 * 64 * (128 + 2) * 4
+    # Split-K over a workspace runs as 1024 equal runs of the (sequence, kv
+    # head, block) order: a partial slot per (sequence, kv head) and per run,
+    # each with G = H_q / H_kv heads of 128 fp32 outputs + (max, sum), then
+    # the block prefix (num_seqs + 1 int32)
+    def balanced(num_seqs, H_q, H_kv):
+        return ((num_seqs * H_kv + 1024) * (H_q // H_kv) * (128 + 2) + num_seqs + 1) * 4
+    assert binding.attn_decode_paged_workspace_size(256, 16, 8, 128, 256, 16) == balanced(256, 16, 8)
+    assert binding.attn_decode_paged_workspace_size(64, 16, 8, 128, 2048, 16) == balanced(64, 16, 8)
+    assert binding.attn_decode_paged_workspace_size(4, 16, 8, 128, 2048, 16) == balanced(4, 16, 8)
+    assert binding.attn_decode_paged_workspace_size(4096, 8, 1, 128, 256, 16) == balanced(4096, 8, 1)
+    # past 4096 sequences (their prefix would not fit LDS), fixed-length
+    # splits: 5000 x 8 pairs, 256-block tables, splits of 128 blocks (2 per
+    # sequence), a slot per (sequence, query head, split)
+    assert binding.attn_decode_paged_workspace_size(5000, 16, 8, 128, 256, 16) == \
+        5000 * 16 * 2 * (128 + 2) * 4
+    # the same when num_seqs * table blocks * H_kv reaches 2^31 (positions of
+    # the order are 32-bit): 4096 x 8 pairs, 65536-block tables, 512 splits
+    assert binding.attn_decode_paged_workspace_size(4096, 16, 8, 128, 65536, 16) == \
+        4096 * 16 * 512 * (128 + 2) * 4
     # a table that fits one split: no workspace
     assert binding.attn_decode_paged_workspace_size(4, 16, 8, 128, 16, 16) == 0
     # invalid or unsupported shapes report 0

@@ -74,6 +74,25 @@ def test_ragged_lengths_and_group_sizes(H_q, H_kv):
     assert_parity(single, ref, "single")
 
 
+# Split-K over a workspace cuts the (sequence, kv head, block) order into
+# equal runs: with few blocks in all, runs of 16 blocks cross many short
+# (sequence, kv head) segments, long sequences span several runs, and empty
+# sequences (in the middle, two in a row, and last) own no blocks at all.
+WALK_LENS = [0, 1, 16, 17, 0, 0, 300, 5, 4000, 33, 0, 2500, 16, 1, 48, 0]
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(16, 8), (8, 1), (6, 2), (4, 4)])
+def test_split_runs_walk_many_segments(H_q, H_kv):
+    q, kc, vc, bt, sl, _, _ = _paged_problem(WALK_LENS, H_q, H_kv, 256, 300 + H_q * 10 + H_kv)
+    say("run walk", H_q, H_kv)
+    live = [i for i, L in enumerate(WALK_LENS) if L > 0]
+    ref = oracle.decode_paged(q, kc, vc, bt, sl, seqs=live)
+    for split in (True, False):
+        got = gpu_decode(q, kc, vc, bt, sl, split)
+        assert np.all(got[[i for i, L in enumerate(WALK_LENS) if L == 0]] == 0.0)
+        assert_parity(got[live], ref, "run walk split" if split else "run walk single")
+
+
 def test_block_permutation_invariance_is_bitwise():
     lens = [700, 33, 1200, 16]
     n, H_q, H_kv, D = len(lens), 16, 8, 128
