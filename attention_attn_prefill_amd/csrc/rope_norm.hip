@@ -64,7 +64,31 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(RopeArgs a) {
   const int64_t token = r / H;
   const int head = (int)(r - token * H);
   half8_t* src = reinterpret_cast<half8_t*>(base + r * D) + sub;
+  // Every load that depends on no other goes out first (the row, its norm
+  // weight, the token's position and slot), the table row as soon as the
+  // position is in: two round trips, not five.
   const half8_t xin = *src;
+  const _Float16* w = kind == 0 ? a.q_weight : a.k_weight;
+  const bool norm = kind != 2 && w != nullptr;
+  half8_t wv = {};
+  if (norm) wv = *(reinterpret_cast<const half8_t*>(w) + sub);
+  const int pos = kind != 2 ? a.positions[token] : 0;
+  int64_t slot = -1;
+  if (APPEND && kind != 0) slot = a.slot_mapping[token];
+  const bool ok = pos >= 0 && pos < a.max_pos;
+  const bool first = sub < LPR / 2;  // elements in [0, D/2)
+  const int i0 = (sub % (LPR / 2)) * 8;
+  float cs[8] = {}, sn[8] = {};
+  if (kind != 2 && ok) {
+    const f32x4_t* ct = reinterpret_cast<const f32x4_t*>(a.cos_table + (int64_t)pos * HALF + i0);
+    const f32x4_t* st = reinterpret_cast<const f32x4_t*>(a.sin_table + (int64_t)pos * HALF + i0);
+    const f32x4_t c0 = ct[0], c1 = ct[1], s0 = st[0], s1 = st[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cs[j] = c0[j]; cs[j + 4] = c1[j];
+      sn[j] = s0[j]; sn[j + 4] = s1[j];
+    }
+  }
 
   half8_t res;
   if (kind == 2) {
@@ -73,32 +97,15 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(RopeArgs a) {
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = (float)xin[j];
-    const _Float16* w = kind == 0 ? a.q_weight : a.k_weight;
-    if (w) {
+    if (norm) {
       float ss = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss = fmaf(y[j], y[j], ss);
 #pragma unroll
       for (int m = 1; m < LPR; m <<= 1) ss += lane_xor(ss, m);
       const float inv = rsqrtf(ss * (1.0f / D) + a.eps);
-      const half8_t wv = *(reinterpret_cast<const half8_t*>(w) + sub);
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = y[j] * inv * (float)wv[j];
-    }
-    const int pos = a.positions[token];
-    const bool first = sub < LPR / 2;  // elements in [0, D/2)
-    const int i0 = (sub % (LPR / 2)) * 8;
-    float cs[8] = {}, sn[8] = {};
-    const bool ok = pos >= 0 && pos < a.max_pos;
-    if (ok) {
-      const f32x4_t* ct = reinterpret_cast<const f32x4_t*>(a.cos_table + (int64_t)pos * HALF + i0);
-      const f32x4_t* st = reinterpret_cast<const f32x4_t*>(a.sin_table + (int64_t)pos * HALF + i0);
-      const f32x4_t c0 = ct[0], c1 = ct[1], s0 = st[0], s1 = st[1];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        cs[j] = c0[j]; cs[j + 4] = c1[j];
-        sn[j] = s0[j]; sn[j + 4] = s1[j];
-      }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -110,7 +117,6 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(RopeArgs a) {
   }
 
   if (APPEND && kind != 0) {
-    const int64_t slot = a.slot_mapping[token];
     if (slot >= 0 && slot < a.num_blocks * (int64_t)a.block_size) {
       const int64_t blk = slot / a.block_size;
       const int off = (int)(slot - blk * a.block_size);
