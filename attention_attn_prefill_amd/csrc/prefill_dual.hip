@@ -542,13 +542,15 @@ struct Dual {
       for (int n = 0; n < K_COPIES; ++n) copy(n, 1, 0);
     }
   }
-  // ROPE: the loads of the row blocks' norm weights, positions and table
-  // rows, and the arithmetic once they (and the Q fragments) are in
-  __device__ __forceinline__ void rope_issue(const PrefillArgs& a) {
-    if constexpr (ROPE) {
-      qr.issue(a, b, row0[0] + col, hf);
-      if (a.positions) qr.tables(a, hf);
-    }
+  // ROPE: the position of the first row block's query row, issued ahead of
+  // the tile loads (the table rows need it, and loads retire in order); then
+  // the norm weights and table rows; the arithmetic once they (and the Q
+  // fragments) are in
+  __device__ __forceinline__ void rope_pos(const PrefillArgs& a) {
+    if constexpr (ROPE) qr.issue_pos(a, b, row0[0] + col);
+  }
+  __device__ __forceinline__ void rope_rest(const PrefillArgs& a) {
+    if constexpr (ROPE) qr.issue_rest(a, hf);
   }
   __device__ __forceinline__ void rope_apply(const PrefillArgs& a) {
     if constexpr (ROPE) {
@@ -556,7 +558,6 @@ struct Dual {
       if (HP == 1) {
         // the second block's rows (32 further on) in turn
         qr.issue(a, b, row0[1] + col, hf);
-        if (a.positions) qr.tables(a, hf);
       }
       q_ok[1] = qr.apply(a, qf[1]);
     }
@@ -681,8 +682,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
   // both tiles read the same K/V rows from key 0 on: the first pass's last
   // two iterations copy the second tile's K(0), V(0), K(1) (see next_base)
   w.next_base = lo < hi ? w.n_tiles : 0x40000000;
+  w.rope_pos(a);
   w.template issue_tile_loads<true>(a);
-  w.rope_issue(a);
+  w.rope_rest(a);
   dev::wait_vmcnt0();
   w.rope_apply(a);
   dev::lds_barrier();
@@ -698,13 +700,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_dual_kernel(PrefillArgs a
     w.setup(a, lo, hg);
     w.par0 = n_first & 1;
     w.next_base = 0x40000000;
+    w.rope_pos(a);  // one register, held across the epilogue
     w.template issue_tile_loads<false>(a);
     const bool full = w.epilogue(a, rows0, heads);
     if (ROPE) {
-      // the rotation's loads go out once the first tile's outputs (and their
-      // registers) are gone; loads retire in order, so waiting for them
-      // waits for the 16 output stores as well
-      w.rope_issue(a);
+      // the rest of the rotation's loads go out once the first tile's
+      // outputs (and their registers) are gone (the position is in by now);
+      // loads retire in order, so waiting for them waits for the 16 output
+      // stores as well
+      w.rope_rest(a);
       dev::wait_vmcnt0();
       w.rope_apply(a);
     } else if (full) {

@@ -431,6 +431,10 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
   p.kv_row_stride = (int64_t)a.H_kv * D;
   p.S_kv = a.S_kv;
 
+  // the row's position goes out first: the table rows need it, and loads
+  // retire in order
+  qnr::QNormRope<D> qr;
+  if constexpr (ROPE) qr.issue_pos(a, b, p.qrow);
   // Q fragment (B operand of S^T = K Q^T): q[qrow][16*ks + 8*hf + 0..7]
   if (p.qrow < a.S_q) {
     const _Float16* qp = a.q + ((int64_t)b * a.S_q + p.qrow) * q_row_stride + (int64_t)h * D + 8 * p.hf;
@@ -440,9 +444,6 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
 #pragma unroll
     for (int ks = 0; ks < P::KS; ++ks) p.qf[ks] = half8_t{};
   }
-  // the row's position and the norm weights go out with the Q loads
-  qnr::QNormRope<D> qr;
-  if constexpr (ROPE) qr.issue(a, b, p.qrow, p.hf);
 #pragma unroll
   for (int dt = 0; dt < P::DT; ++dt) p.o[dt] = f32x16_t{};
   p.m = -INFINITY;  // reference point of the exponentials (raw dot-product units)
@@ -470,9 +471,7 @@ __device__ __forceinline__ void prefill_qtile(const PrefillArgs& a, int qt, int 
 
   // prologue: K(0), V(0) and K(1) into LDS
   p.st.init(p.kbase, p.vbase, (int)p.kv_row_stride, a.S_kv);
-  if constexpr (ROPE) {
-    if (a.positions) qr.tables(a, p.hf);  // as soon as the position is in
-  }
+  if constexpr (ROPE) qr.issue_rest(a, p.hf);  // the weights and table rows
   // K(0), V(0) and K(1) in flight together: one global round trip
   half8_t k1[Stager<D, HP>::PER_T];
   p.st.load_k(0, p.tid);
@@ -636,7 +635,6 @@ hipError_t launch_prefill(const PrefillArgs& a_in, int head_dim, bool causal, hi
   switch (head_dim) {
     case 32: return causal ? launch_hp<32, true>(a, stream) : launch_hp<32, false>(a, stream);
     case 64: return causal ? launch_hp<64, true>(a, stream) : launch_hp<64, false>(a, stream);
-    case 128: return causal ? launch_hp<128, true>(a, stream) : launch_hp<128, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

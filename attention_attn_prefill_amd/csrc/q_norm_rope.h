@@ -19,10 +19,10 @@ __device__ __forceinline__ float half_swap_add(float x) {
 // RMSNorm (when q_weight is set) and NeoX rotation of the Q fragment of one
 // lane (dims 16 ks + 8 hf + j of its query row), in fp32, rounded to fp16
 // once.  Its loads go out in two waves so that their latency overlaps the
-// first K/V tile loads: the weight slices and the position with the Q loads
-// (issue), the table rows once the position is known (tables), then the
+// first K/V tile loads: the position (issue_pos), then the weight slices and
+// the table rows once the position is known (issue_rest), then the
 // arithmetic (apply).  Without a positions array the position is the row's
-// index in its sequence and the table rows go out with the Q loads too.
+// index in its sequence.
 // Rows past S_q stay zero.  apply() returns false for a position outside
 // [0, max_pos): that row's fragment is zero (the kernels using this are
 // built without NaN semantics, so no NaN enters the arithmetic) and their
@@ -37,13 +37,20 @@ struct QNormRope {
   bool valid, ok;
 
   __device__ __forceinline__ void issue(const PrefillArgs& a, int b, int qrow, int hf) {
+    issue_pos(a, b, qrow);
+    issue_rest(a, hf);
+  }
+  // The two halves of issue().  A kernel that issues its tile loads in
+  // between should take the position first: loads retire in order, so the
+  // table rows, which need the position, would otherwise wait for every
+  // tile load issued ahead of it.
+  __device__ __forceinline__ void issue_pos(const PrefillArgs& a, int b, int qrow) {
     valid = qrow < a.S_q;
-    if (a.positions) {
-      pos = valid ? a.positions[(int64_t)b * a.S_q + qrow] : 0;
-    } else {
-      pos = qrow;
-      tables(a, hf);
-    }
+    if (a.positions) pos = valid ? a.positions[(int64_t)b * a.S_q + qrow] : 0;
+    else pos = qrow;
+  }
+  __device__ __forceinline__ void issue_rest(const PrefillArgs& a, int hf) {
+    tables(a, hf);
     if (a.q_weight) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const half8_t*>(a.q_weight + 16 * ks + 8 * hf);
