@@ -62,6 +62,10 @@ def parse():
                         "(S = 1024/2048/4096/8192, B = 8/4/2/1, H_q 16, H_kv 8), whose "
                         "workgroups run 18/34/66/130 64-key iterations, and the fit "
                         "time = fixed + iterations x per-iteration cost")
+    p.add_argument("--operand-clock", action="store_true",
+                   help="instead of the step: fp16 rates of the vendor GEMM (torch.matmul, "
+                        "8192^3) and of the causal prefill (qwen3_prefill, long_prefill), "
+                        "each on N(0,1) operands and on all-zero operands")
     return p.parse_args()
 
 
@@ -509,6 +513,58 @@ def main_sweep(args):
                                             "us_per_iteration": round(float(c), 4)}}))
 
 
+def main_operand_clock(args):
+    """How far the dense fp16 peak is reachable on this chip.  The peak
+    assumes 2.4 GHz; under the power drawn by busy matrix cores the chip
+    lowers its clock, and the draw depends on the operand bits.  The same
+    launches are timed on N(0,1) operands and on all-zero operands (same
+    instructions, same bytes): the vendor GEMM (torch.matmul on fp16,
+    8192 x 8192 x 8192) and the causal prefill of both workloads.  Times are
+    the pages' method (HIP events around back-to-back launches, median of 5)."""
+    import torch
+
+    from attention_attn_prefill_amd import attn_prefill
+    from attention_attn_prefill_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+
+    def timed(name, kind, fn, flops, iters):
+        t0 = time.time()
+        while time.time() - t0 < 1.0:
+            fn()
+        torch.cuda.synchronize()
+        ms, _ = pages_method(fn, stream, iters=iters, warm=args.warmup, repeats=5)
+        tf = flops / ms / 1e9
+        rows.append({"op": name, "operands": kind, "us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_FP16_TFLOPS, 4)})
+        print(f"[operand-clock] {name} {kind}: {ms * 1e3:.2f} us, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    n = 8192
+    a = torch.from_numpy(W.normal_f16((n, n), [31, 1])).to(dev)
+    b = torch.from_numpy(W.normal_f16((n, n), [31, 2])).to(dev)
+    c = torch.empty((n, n), dtype=torch.float16, device=dev)
+    for kind in ("normal", "zeros"):
+        if kind == "zeros":
+            a.zero_()
+            b.zero_()
+        timed("matmul_8192", kind, lambda: torch.matmul(a, b, out=c), 2.0 * n ** 3, 20)
+    del a, b, c
+    for name, iters in (("qwen3_prefill", 100), ("long_prefill", 5)):
+        cfg = W.CONFIGS[name]
+        q, k, v = (torch.from_numpy(x).to(dev) for x in W.prefill_inputs(cfg))
+        o = torch.empty_like(q)
+        for kind in ("normal", "zeros"):
+            if kind == "zeros":
+                for x in (q, k, v):
+                    x.zero_()
+            timed(name, kind, lambda: attn_prefill(q, k, v, o, causal=True), cfg.flops, iters)
+        del q, k, v, o
+    print(json.dumps({"mode": "operand_clock", "peak_tflops": PEAK_FP16_TFLOPS,
+                      "method": "HIP events around back-to-back launches, median of 5", "rows": rows}))
+
+
 def calibration_copy(dev):
     import torch
     src = torch.ones(256 << 20, dtype=torch.float16, device=dev)
@@ -528,6 +584,9 @@ def main():
 
     if args.prefill_sweep:
         main_sweep(args)
+        return
+    if args.operand_clock:
+        main_operand_clock(args)
         return
     if args.workload == "grpo":
         main_grpo(args)
