@@ -615,11 +615,15 @@ struct Dual {
       half8_t v8[PER_G];
 #pragma unroll
       for (int i = 0; i < PER_G; ++i) v8[i] = *reinterpret_cast<const half8_t*>(ot + (i * ROWS_PER + pr) * OROW + 8 * pc);
+      // non-temporal stores: nothing in this launch reads the output back,
+      // so it need not stay in L2 next to the K/V rows, nor be held there
+      // until the write-back at the kernel's end
 #pragma unroll
       for (int i = 0; i < PER_G; ++i) {
         const int row = rows0[g] + i * ROWS_PER + pr;
         if (full || row < a.S_q)
-          *reinterpret_cast<half8_t*>(a.o + ((int64_t)b * a.S_q + row) * q_row_stride + (int64_t)heads[g] * D + 8 * pc) = v8[i];
+          __builtin_nontemporal_store(
+              v8[i], reinterpret_cast<half8_t*>(a.o + ((int64_t)b * a.S_q + row) * q_row_stride + (int64_t)heads[g] * D + 8 * pc));
       }
     }
     return full;
