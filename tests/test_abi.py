@@ -75,6 +75,11 @@ def prefill(lib, q=P, k=P, v=P, o=P2, B=1, S_q=64, S_kv=64, H_q=2, H_kv=1, D=128
     (dict(S_q=64, S_kv=65, causal=1), INV),
     (dict(D=96), UNS), (dict(D=256), UNS), (dict(D=0), INV),
     (dict(S_q=1, S_kv=1 << 20, H_q=8, H_kv=8, causal=0), UNS),   # K of one batch entry >= 2 GiB
+    # one key past the largest K/V that 32-bit offsets allow with the three
+    # staged tiles past the end: (ceil(S_kv / 64) + 3) * 64 * H_kv * D * 2 >= 2^31
+    # (the GPU parity test runs at the largest accepted S_kv)
+    (dict(S_q=1, S_kv=8388352 + 1, H_q=2, H_kv=1, causal=0), UNS),
+    (dict(S_q=1, S_kv=16776960 + 1, H_q=2, H_kv=1, D=64, causal=0), UNS),
     (dict(q=ctypes.c_void_p(0x10008)), INV), (dict(o=ctypes.c_void_p(0x20002)), INV),
 ])
 def test_prefill_rejects(lib, kw, want):

@@ -164,6 +164,44 @@ def test_long_prefill_full_size_sampled_rows():
     assert_parity(got[rows], ref, "long_prefill")
 
 
+def _max_s_kv(H_kv, D):
+    """Largest S_kv the host accepts: K/V rows of one batch entry are addressed
+    with 32-bit byte offsets, and the kernels stage up to three 64-key tiles
+    past the last one, so (ceil(S_kv / 64) + 3) * 64 * H_kv * D * 2 < 2^31."""
+    return (((1 << 31) - 1) // (64 * H_kv * D * 2) - 3) * 64
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("D,short", [(128, 5), (64, 0)])
+def test_non_causal_at_the_kv_offset_limit(D, short):
+    """The largest K/V that the 32-bit offsets allow (one kv head, 2.1 GB each
+    of K and V): 40 query rows of two heads against every key.  Scores near 0
+    for the bulk of the keys would make the output an average of millions of
+    rows, near zero whatever keys were read, so eight needle keys spread over
+    the whole range, the last one at the end of the buffer, score far above
+    the rest (q[..., 0] = 8, the needle's k[0] = 32 down to 28.5) and carry
+    graded weights.  A missed or misplaced needle moves the output by several
+    percent.  Every row of two heads at the first and last four query
+    positions against the oracle."""
+    S_kv = _max_s_kv(1, D) - short
+    B, S_q, H_q, H_kv = 1, 40, 2, 1
+    q = _rand((B, S_q, H_q, D), 71)
+    q[..., 0] = 8
+    k = _rand((B, S_kv, H_kv, D), 72)
+    k *= np.float16(0.1)
+    needles = [3, 64 * 1000 + 17, S_kv // 3, S_kv // 2 + 1, S_kv - 64 * 7 - 2, S_kv - 65, S_kv - 2, S_kv - 1]
+    for i, j in enumerate(needles):
+        k[0, j, 0, 0] = 32.0 - 0.5 * i
+    v = _rand((B, S_kv, H_kv, D), 73)
+    say("kv offset limit", D, S_kv)
+    got = gpu_prefill(q, k, v, False).reshape(-1, D)
+    pos = np.array([0, 1, 2, 3, S_q - 4, S_q - 3, S_q - 2, S_q - 1], np.int64)
+    rows = np.concatenate([pos * H_q + h for h in range(H_q)])
+    ref = oracle.prefill(q, k, v, False, rows=rows)
+    assert np.abs(ref).max() > 0.1  # the needles dominate
+    assert_parity(got[rows], ref, f"kv offset limit D={D}")
+
+
 # ---- invariants on the GPU output ------------------------------------------
 
 def test_values_one_give_one():
