@@ -95,6 +95,29 @@ def test_split_runs_walk_many_segments(H_q, H_kv):
         assert_parity(got[live], ref, "run walk split" if split else "run walk single")
 
 
+# Beyond 4096 sequences the balanced mode (whose per-sequence cost prefix
+# lives in LDS) gives way to fixed-length splits of 128 blocks, each with its
+# own partial slot, and the merge kernel for sequences longer than one split.
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("H_q,H_kv", [(16, 8), (8, 1)])
+def test_fixed_splits_beyond_the_balanced_limit(H_q, H_kv):
+    n, max_bps, D = 5000, 256, 128
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([97, H_q, H_kv])))
+    lens = g.integers(1, 64, size=n, endpoint=True)
+    lens[::499] = g.integers(2049, 4096, size=len(lens[::499]), endpoint=True)  # two splits each
+    lens[7] = 2048  # exactly one full split
+    lens = lens.astype(np.int32)
+    bt, num_blocks = W.paged_layout(lens, 16, max_bps, (97, H_q, H_kv, 1))
+    q = _rand((n, H_q, D), 400 + H_q + H_kv)
+    kc = _rand((num_blocks, H_kv, 16, D), 401 + H_q + H_kv)
+    vc = _rand((num_blocks, H_kv, 16, D), 402 + H_q + H_kv)
+    say("fixed splits", n, H_q, H_kv, num_blocks)
+    ref = oracle.decode_paged(q, kc, vc, bt, lens)
+    for split in (True, False):
+        assert_parity(gpu_decode(q, kc, vc, bt, lens, split), ref,
+                      "fixed splits" if split else "fixed splits single")
+
+
 def test_block_permutation_invariance_is_bitwise():
     lens = [700, 33, 1200, 16]
     n, H_q, H_kv, D = len(lens), 16, 8, 128
