@@ -6,7 +6,8 @@
 // skipped).  Token i's rows k_new[i, h, :] / v_new[i, h, :] go to
 // cache[slot / block_size, h, slot % block_size, :].
 //
-// Pure data movement, HBM-bound: every byte is read once and written once.
+// Pure data movement, HBM-bound: every byte is read once and written once,
+// by non-temporal loads and stores.
 // One wavefront per token; its H_kv * D halfs are moved as 16-byte vectors,
 // lane-contiguous on the read side (the token's rows are contiguous) and
 // 16 lanes per 2*D-byte cache row on the write side.  Slots outside
@@ -38,8 +39,10 @@ __global__ __launch_bounds__(64 * kWaves) void kv_append_kernel(KvAppendArgs a) 
     const int64_t dst = ((block * a.H_kv + h) * a.block_size + off) * a.head_dim + 8 * c;
     const half8_t kx = __builtin_nontemporal_load(ks + v);
     const half8_t vx = __builtin_nontemporal_load(vs + v);
-    *reinterpret_cast<half8_t*>(a.k_cache + dst) = kx;
-    *reinterpret_cast<half8_t*>(a.v_cache + dst) = vx;
+    // non-temporal both ways: this launch touches each byte once, and the
+    // cache rows are read by later calls, not from this launch's L2
+    __builtin_nontemporal_store(kx, reinterpret_cast<half8_t*>(a.k_cache + dst));
+    __builtin_nontemporal_store(vx, reinterpret_cast<half8_t*>(a.v_cache + dst));
   }
 }
 
