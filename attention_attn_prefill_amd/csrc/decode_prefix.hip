@@ -235,10 +235,11 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_chunk_kernel(DecodeArgs a,
     for (int j = 0; j < kLoads; ++j) {
       // this load's rows lie in block (kRowsPerWave * wave + 4 j) / 16 of the pair
       const int64_t blk = ((kRowsPerWave * wave + 4 * j) < 16 ? e0 : e1) * slab + head_off;
+      // non-temporal (aux = 2): each slab is read once per launch
       __builtin_amdgcn_raw_ptr_buffer_load_lds(slab_rsrc(a.k_cache + blk), LDS_PTR(kd + 4 * j * D), 16,
-                                               voff_k[j], 0, 0, 0);
+                                               voff_k[j], 0, 0, 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(slab_rsrc(a.v_cache + blk), LDS_PTR(vd + 4 * j * D), 16,
-                                               voff_v[j], 0, 0, 0);
+                                               voff_v[j], 0, 0, 2);
     }
   };
 
