@@ -113,7 +113,9 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(RopeArgs a) {
       const float o = first ? fmaf(y[j], cs[j], -p * sn[j]) : fmaf(y[j], cs[j], p * sn[j]);
       res[j] = (_Float16)(ok ? o : __builtin_nanf(""));
     }
-    *src = res;  // in place
+    // non-temporal stores (in place and into the cache): nothing in this
+    // launch reads them back
+    __builtin_nontemporal_store(res, src);
   }
 
   if (APPEND && kind != 0) {
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(RopeArgs a) {
       const int64_t blk = slot / a.block_size;
       const int off = (int)(slot - blk * a.block_size);
       _Float16* cache = kind == 1 ? a.k_cache : a.v_cache;
-      *(reinterpret_cast<half8_t*>(cache + ((blk * a.H_kv + head) * a.block_size + off) * D) + sub) = res;
+      __builtin_nontemporal_store(res, reinterpret_cast<half8_t*>(cache + ((blk * a.H_kv + head) * a.block_size + off) * D) + sub);
     }
   }
 }
